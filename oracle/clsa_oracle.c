@@ -98,6 +98,20 @@ static double orc_decode_e4m3fn(uint8_t b) {
   return sign ? -v : v;
 }
 
+/* Value tables of the two 16-/8-bit formats, filled once from the field
+ * decoders above (the oracle is single-threaded; tables are filled on the
+ * first call of each entry point). */
+static double orc_bf16_table[65536];
+static double orc_e4m3fn_table[256];
+static int orc_tables_ready = 0;
+
+static void orc_init_tables(void) {
+  if (orc_tables_ready) return;
+  for (uint32_t h = 0; h < 65536; h++) orc_bf16_table[h] = orc_decode_bf16((uint16_t)h);
+  for (uint32_t b = 0; b < 256; b++) orc_e4m3fn_table[b] = orc_decode_e4m3fn((uint8_t)b);
+  orc_tables_ready = 1;
+}
+
 /* Element i of a buffer of the given type. */
 static double orc_elem(const void* base, size_t i, int dtype) {
   if (dtype == ORC_F32) {
@@ -108,15 +122,21 @@ static double orc_elem(const void* base, size_t i, int dtype) {
   if (dtype == ORC_BF16) {
     uint16_t h;
     memcpy(&h, (const unsigned char*)base + 2 * i, 2);
-    return orc_decode_bf16(h);
+    return orc_bf16_table[h];
   }
-  return orc_decode_e4m3fn(((const uint8_t*)base)[i]);
+  return orc_e4m3fn_table[((const uint8_t*)base)[i]];
 }
 
 /* Decode n elements into doubles (exported so tests can pin the decoders
  * against independent conversions). */
 void orc_decode(const void* src, int dtype, long n, double* dst) {
+  orc_init_tables();
   for (long i = 0; i < n; i++) dst[i] = orc_elem(src, (size_t)i, dtype);
+}
+
+/* Decode the n elements starting at element `first` (one row). */
+static void orc_row(const void* base, size_t first, int n, int dtype, double* dst) {
+  for (int i = 0; i < n; i++) dst[i] = orc_elem(base, first + (size_t)i, dtype);
 }
 
 /* Number of cache positions query t of a T-query call sees. */
@@ -141,9 +161,19 @@ int orc_index_score(const void* q, const void* k, int dtype, const float* w,
                     double* scores, double* bound, int B, int T, int H, int D,
                     int kv_len, int L_cap) {
   if (B < 1 || T < 1 || H < 1 || D < 1 || kv_len < T || L_cap < kv_len) return -1;
+  orc_init_tables();
+  double* qd = (double*)malloc(sizeof(double) * (size_t)H * D);
+  double* kd = (double*)malloc(sizeof(double) * (size_t)D);
+  if (!qd || !kd) {
+    free(qd);
+    free(kd);
+    return -2;
+  }
   for (int b = 0; b < B; b++) {
     for (int t = 0; t < T; t++) {
       long vis = orc_visible(kv_len, T, t);
+      orc_row(q, ((size_t)b * T + t) * H * D, H * D, dtype, qd);
+      const float* wr = w + ((size_t)b * T + t) * H;
       for (long s = 0; s < kv_len; s++) {
         size_t o = ((size_t)b * T + t) * kv_len + s;
         if (s >= vis) {
@@ -151,16 +181,15 @@ int orc_index_score(const void* q, const void* k, int dtype, const float* w,
           if (bound) bound[o] = 0.0;
           continue;
         }
+        orc_row(k, ((size_t)b * L_cap + s) * D, D, dtype, kd);
         double total = 0.0, mag = 0.0;
         for (int h = 0; h < H; h++) {
           double dot = 0.0, adot = 0.0;
           for (int d = 0; d < D; d++) {
-            double qv = orc_elem(q, (((size_t)b * T + t) * H + h) * D + d, dtype);
-            double kv = orc_elem(k, ((size_t)b * L_cap + s) * D + d, dtype);
-            dot += qv * kv;
-            adot += fabs(qv * kv);
+            dot += qd[h * D + d] * kd[d];
+            adot += fabs(qd[h * D + d] * kd[d]);
           }
-          double wh = (double)w[((size_t)b * T + t) * H + h];
+          double wh = (double)wr[h];
           total += wh * (dot > 0.0 ? dot : 0.0);
           mag += fabs(wh) * adot;
         }
@@ -169,6 +198,8 @@ int orc_index_score(const void* q, const void* k, int dtype, const float* w,
       }
     }
   }
+  free(qd);
+  free(kd);
   return 0;
 }
 
@@ -251,29 +282,35 @@ int orc_sparse_attn(const void* q, const void* kc, const void* vc, int dtype,
   if (B < 1 || T < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv || D < 1 || k < 1 ||
       kv_len < T || L_cap < kv_len)
     return -1;
+  orc_init_tables();
   if (scale <= 0.0) scale = 1.0 / sqrt((double)D);
   int G = Hq / Hkv;
   double* z = (double*)malloc(sizeof(double) * (size_t)k);
-  if (!z) return -2;
+  double* qd = (double*)malloc(sizeof(double) * (size_t)D);
+  double* row = (double*)malloc(sizeof(double) * (size_t)D);
+  if (!z || !qd || !row) {
+    free(z);
+    free(qd);
+    free(row);
+    return -2;
+  }
   for (int b = 0; b < B; b++) {
     for (int t = 0; t < T; t++) {
       long vis = orc_visible(kv_len, T, t);
-      const int32_t* row = idx + ((size_t)b * T + t) * k;
+      const int32_t* sel = idx + ((size_t)b * T + t) * k;
       for (int h = 0; h < Hq; h++) {
         int g = h / G;
+        orc_row(q, (((size_t)b * T + t) * Hq + h) * D, D, dtype, qd);
         double* o = out + (((size_t)b * T + t) * Hq + h) * D;
         for (int d = 0; d < D; d++) o[d] = 0.0;
         double m = -INFINITY;
         int nvalid = 0;
         for (int j = 0; j < k; j++) {
-          long s = row[j];
+          long s = sel[j];
           if (s < 0 || s >= vis) continue;
+          orc_row(kc, (((size_t)b * L_cap + s) * Hkv + g) * D, D, dtype, row);
           double dot = 0.0;
-          for (int d = 0; d < D; d++) {
-            double qv = orc_elem(q, (((size_t)b * T + t) * Hq + h) * D + d, dtype);
-            double kv = orc_elem(kc, (((size_t)b * L_cap + s) * Hkv + g) * D + d, dtype);
-            dot += qv * kv;
-          }
+          for (int d = 0; d < D; d++) dot += qd[d] * row[d];
           z[j] = scale * dot;
           if (z[j] > m) m = z[j];
           nvalid++;
@@ -285,12 +322,12 @@ int orc_sparse_attn(const void* q, const void* kc, const void* vc, int dtype,
         }
         double l = 0.0;
         for (int j = 0; j < k; j++) {
-          long s = row[j];
+          long s = sel[j];
           if (s < 0 || s >= vis) continue;
           double p = exp(z[j] - m);
           l += p;
-          for (int d = 0; d < D; d++)
-            o[d] += p * orc_elem(vc, (((size_t)b * L_cap + s) * Hkv + g) * D + d, dtype);
+          orc_row(vc, (((size_t)b * L_cap + s) * Hkv + g) * D, D, dtype, row);
+          for (int d = 0; d < D; d++) o[d] += p * row[d];
         }
         for (int d = 0; d < D; d++) o[d] /= l;
         *l_out = m + log(l);
@@ -298,6 +335,8 @@ int orc_sparse_attn(const void* q, const void* kc, const void* vc, int dtype,
     }
   }
   free(z);
+  free(qd);
+  free(row);
   return 0;
 }
 
@@ -405,6 +444,7 @@ int orc_block_attn(const void* q, const void* kc, const void* vc, int dtype,
   if (B < 1 || T < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv || D < 1 || block < 1 ||
       kv_len < T || L_cap < kv_len)
     return -1;
+  orc_init_tables();
   if (scale <= 0.0) scale = 1.0 / sqrt((double)D);
   int G = Hq / Hkv;
   double* z = (double*)malloc(sizeof(double) * (size_t)kv_len);

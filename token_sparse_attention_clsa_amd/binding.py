@@ -1,0 +1,318 @@
+"""ctypes binding of libclsa.so, one function per C entry point.
+
+Argument marshalling only: tensors are checked for device, dtype, shape and
+contiguity, their device pointers and torch's current HIP stream are passed
+to the C ABI, and a non-zero status raises ClsaError with the library's own
+message. Every step of the computation runs in the HIP kernels; there is no
+fallback path. Torch provides device memory (outputs and workspaces are
+torch tensors) and the stream.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import re
+from typing import List, Optional, Sequence
+
+import torch  # loads torch's HIP runtime first; libclsa binds to the same one
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libclsa.so")
+HEADER = os.path.join(os.path.dirname(_HERE), "include", "clsa.h")
+
+F32, BF16, FP8_E4M3FN = 0, 1, 2
+OP_TOPK, OP_SPARSE_ATTN, OP_BLOCK_UNION = 0, 1, 2
+_DT = {torch.float32: F32, torch.bfloat16: BF16, torch.float8_e4m3fn: FP8_E4M3FN}
+
+P, I, F, SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+
+
+class ClsaError(RuntimeError):
+    def __init__(self, status: int, where: str, message: str):
+        super().__init__(f"{where}: {message} (status {status})")
+        self.status = status
+
+
+class StepDesc(ctypes.Structure):
+    _fields_ = [
+        ("n_layers", I),
+        ("layer_src", ctypes.POINTER(ctypes.c_int32)),
+        ("q", ctypes.POINTER(P)),
+        ("k_cache", ctypes.POINTER(P)),
+        ("v_cache", ctypes.POINTER(P)),
+        ("out", ctypes.POINTER(P)),
+        ("lse", ctypes.POINTER(P)),
+        ("q_idx", ctypes.POINTER(P)),
+        ("k_idx", ctypes.POINTER(P)),
+        ("w", ctypes.POINTER(P)),
+        ("idx_out", P),
+        ("dtype", I),
+        ("idx_dtype", I),
+        ("B", I), ("T", I), ("Hq", I), ("Hkv", I), ("D", I), ("H_I", I), ("D_I", I),
+        ("kv_len", I), ("L_cap", I), ("k", I),
+        ("scale", F),
+        ("events", ctypes.POINTER(P)),
+    ]
+
+
+_lib = None
+
+
+def load() -> ctypes.CDLL:
+    """Load libclsa.so (built in-tree by build.py). Raises if it is missing."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build it with `python -m token_sparse_attention_clsa_amd.build` "
+            "(the CLSA ops have no fallback path)")
+    lib = ctypes.CDLL(LIB_PATH)
+    sig = {
+        "clsa_abi_version": (I, []),
+        "clsa_status_string": (ctypes.c_char_p, [I]),
+        "clsa_last_error": (ctypes.c_char_p, []),
+        "clsa_workspace_bytes": (SZ, [I] * 9),
+        "clsa_index_score": (I, [P, P, I, P, P] + [I] * 6 + [P]),
+        "clsa_topk": (I, [P, I, I, I, I, P, P, SZ, P]),
+        "clsa_sparse_attn": (I, [P, P, P, I, P, I, P, P] + [I] * 7 + [F, P, SZ, P]),
+        "clsa_decode_step_workspace_bytes": (SZ, [ctypes.POINTER(StepDesc)]),
+        "clsa_decode_step": (I, [ctypes.POINTER(StepDesc), P, SZ, P]),
+        "clsa_block_union_build": (I, [P] + [I] * 6 + [P, P, P, SZ, P]),
+        "clsa_block_paged_attn": (I, [P, P, P, I, P, P, I, P, P] + [I] * 7 + [F, P]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def declared_symbols() -> List[str]:
+    """Entry points declared in include/clsa.h."""
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(clsa_[a-z_0-9]+)\s*\(", text)))
+
+
+def _check(rc: int, where: str) -> None:
+    if rc != 0:
+        lib = load()
+        raise ClsaError(rc, where, lib.clsa_last_error().decode())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dev(t: torch.Tensor, name: str, dtypes=None, shape=None):
+    if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+        raise ValueError(f"{name} must be a CUDA (HIP) tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtypes is not None and t.dtype not in dtypes:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    return t
+
+
+def workspace_bytes(op: int, B=0, T=0, Hq=0, Hkv=0, D=0, kv_len=0, k=0, block=0) -> int:
+    return int(load().clsa_workspace_bytes(op, B, T, Hq, Hkv, D, kv_len, k, block))
+
+
+def _workspace(nbytes: int, device) -> torch.Tensor:
+    return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+
+
+# ----------------------------------------------------------------------------
+# Entry points
+# ----------------------------------------------------------------------------
+
+def index_score(q_idx: torch.Tensor, k_idx: torch.Tensor, w: torch.Tensor, kv_len: Optional[int] = None,
+                out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """clsa_index_score. q_idx [B,T,H_I,D_I], k_idx [B,L_cap,D_I], w [B,T,H_I] -> [B,T,kv_len] f32."""
+    _dev(q_idx, "q_idx", _DT)
+    B, T, H, D = q_idx.shape
+    _dev(k_idx, "k_idx", (q_idx.dtype,))
+    L_cap = k_idx.shape[1]
+    _dev(k_idx, "k_idx", shape=(B, L_cap, D))
+    _dev(w, "w", (torch.float32,), (B, T, H))
+    kv_len = L_cap if kv_len is None else kv_len
+    if out is None:
+        out = torch.empty((B, T, kv_len), dtype=torch.float32, device=q_idx.device)
+    _dev(out, "scores", (torch.float32,), (B, T, kv_len))
+    rc = load().clsa_index_score(_ptr(q_idx), _ptr(k_idx), _DT[q_idx.dtype], _ptr(w), _ptr(out),
+                                 B, T, H, D, kv_len, L_cap, _stream())
+    _check(rc, "clsa_index_score")
+    return out
+
+
+def topk(scores: torch.Tensor, k: int, out: Optional[torch.Tensor] = None,
+         ws: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """clsa_topk. scores [B,T,kv_len] f32 -> idx [B,T,k] int32 (ascending, -1 padded)."""
+    _dev(scores, "scores", (torch.float32,))
+    B, T, L = scores.shape
+    if out is None:
+        out = torch.empty((B, T, k), dtype=torch.int32, device=scores.device)
+    _dev(out, "idx", (torch.int32,), (B, T, k))
+    need = workspace_bytes(OP_TOPK, B=B, T=T, kv_len=L, k=k)
+    if ws is None:
+        ws = _workspace(need, scores.device)
+    rc = load().clsa_topk(_ptr(scores), B, T, L, k, _ptr(out), _ptr(ws), ws.numel(), _stream())
+    _check(rc, "clsa_topk")
+    return out
+
+
+def sparse_attn(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, idx: torch.Tensor,
+                kv_len: Optional[int] = None, scale: float = 0.0, out: Optional[torch.Tensor] = None,
+                lse: Optional[torch.Tensor] = None, want_lse: bool = True,
+                ws: Optional[torch.Tensor] = None):
+    """clsa_sparse_attn. Returns (out [B,T,Hq,D], lse [B,T,Hq] f32 or None)."""
+    _dev(q, "q", (torch.float32, torch.bfloat16))
+    B, T, Hq, D = q.shape
+    L_cap, Hkv = k_cache.shape[1], k_cache.shape[2]
+    _dev(k_cache, "k_cache", (q.dtype,), (B, L_cap, Hkv, D))
+    _dev(v_cache, "v_cache", (q.dtype,), (B, L_cap, Hkv, D))
+    _dev(idx, "idx", (torch.int32,))
+    k = idx.shape[2]
+    _dev(idx, "idx", shape=(B, T, k))
+    kv_len = L_cap if kv_len is None else kv_len
+    if out is None:
+        out = torch.empty_like(q)
+    _dev(out, "out", (q.dtype,), q.shape)
+    if lse is None and want_lse:
+        lse = torch.empty((B, T, Hq), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _dev(lse, "lse", (torch.float32,), (B, T, Hq))
+    need = workspace_bytes(OP_SPARSE_ATTN, B=B, T=T, Hq=Hq, Hkv=Hkv, D=D, k=k)
+    if ws is None:
+        ws = _workspace(need, q.device)
+    rc = load().clsa_sparse_attn(_ptr(q), _ptr(k_cache), _ptr(v_cache), _DT[q.dtype], _ptr(idx), k,
+                                 _ptr(out), _ptr(lse), B, T, Hq, Hkv, D, kv_len, L_cap, float(scale),
+                                 _ptr(ws), ws.numel(), _stream())
+    _check(rc, "clsa_sparse_attn")
+    return out, lse
+
+
+class DecodeStep:
+    """A reusable clsa_decode_step call: descriptor, outputs and workspace built once.
+
+    layer_src: F/S layer map (layer_src[l] == l marks an F layer).
+    Per-layer lists: q, k_cache, v_cache; indexer lists q_idx, k_idx, w hold
+    tensors on F layers and None on S layers. ``run()`` enqueues one step on
+    torch's current stream; outputs live in ``self.out`` / ``self.lse`` and the
+    index cache in ``self.idx``.
+    """
+
+    def __init__(self, layer_src: Sequence[int], q, k_cache, v_cache, q_idx, k_idx, w, k: int,
+                 kv_len: Optional[int] = None, scale: float = 0.0, want_lse: bool = True,
+                 events: Optional[Sequence] = None):
+        n = len(layer_src)
+        self.n = n
+        dev = q[0].device
+        B, T, Hq, D = q[0].shape
+        L_cap, Hkv = k_cache[0].shape[1], k_cache[0].shape[2]
+        kv_len = L_cap if kv_len is None else kv_len
+        f0 = next((i for i in range(n) if q_idx[i] is not None), None)
+        if f0 is None:
+            raise ValueError("decode step needs at least one full (indexer) layer")
+        H_I, D_I = q_idx[f0].shape[2], q_idx[f0].shape[3]
+        for l in range(n):
+            _dev(q[l], f"q[{l}]", (torch.float32, torch.bfloat16), (B, T, Hq, D))
+            _dev(k_cache[l], f"k_cache[{l}]", (q[0].dtype,), (B, L_cap, Hkv, D))
+            _dev(v_cache[l], f"v_cache[{l}]", (q[0].dtype,), (B, L_cap, Hkv, D))
+            if q_idx[l] is not None:
+                _dev(q_idx[l], f"q_idx[{l}]", (q_idx[f0].dtype,), (B, T, H_I, D_I))
+                _dev(k_idx[l], f"k_idx[{l}]", (q_idx[f0].dtype,), (B, L_cap, D_I))
+                _dev(w[l], f"w[{l}]", (torch.float32,), (B, T, H_I))
+        self._keep = [q, k_cache, v_cache, q_idx, k_idx, w]
+        self.out = [torch.empty_like(q[l]) for l in range(n)]
+        self.lse = [torch.empty((B, T, Hq), dtype=torch.float32, device=dev) for _ in range(n)] \
+            if want_lse else None
+        self.idx = torch.empty((B, T, k), dtype=torch.int32, device=dev)
+        PA = P * n
+        self._src = (ctypes.c_int32 * n)(*layer_src)
+        self._q = PA(*[t.data_ptr() for t in q])
+        self._k = PA(*[t.data_ptr() for t in k_cache])
+        self._v = PA(*[t.data_ptr() for t in v_cache])
+        self._o = PA(*[t.data_ptr() for t in self.out])
+        self._lse = PA(*[t.data_ptr() for t in self.lse]) if want_lse else None
+        self._qi = PA(*[0 if t is None else t.data_ptr() for t in q_idx])
+        self._ki = PA(*[0 if t is None else t.data_ptr() for t in k_idx])
+        self._w = PA(*[0 if t is None else t.data_ptr() for t in w])
+        self._ev = None
+        if events is not None:
+            if len(events) != 4 * n:
+                raise ValueError("events must hold 4 * n_layers torch.cuda.Event objects")
+            for e in events:
+                if e.cuda_event == 0:   # torch creates the handle at first record
+                    e.record()
+            self._ev = (P * (4 * n))(*[e.cuda_event for e in events])
+        self.desc = StepDesc(
+            n, self._src, self._q, self._k, self._v, self._o,
+            self._lse if self._lse is not None else ctypes.POINTER(P)(),
+            self._qi, self._ki, self._w, self.idx.data_ptr(),
+            _DT[q[0].dtype], _DT[q_idx[f0].dtype], B, T, Hq, Hkv, D, H_I, D_I, kv_len, L_cap, k,
+            float(scale), self._ev if self._ev is not None else ctypes.POINTER(P)())
+        lib = load()
+        need = lib.clsa_decode_step_workspace_bytes(ctypes.byref(self.desc))
+        if need == 0:
+            lib.clsa_decode_step(ctypes.byref(self.desc), None, 0, None)  # sets the error text
+            _check(-1, "clsa_decode_step")
+        self.ws = _workspace(int(need), dev)
+        self._fn = lib.clsa_decode_step
+        self._desc_ref = ctypes.byref(self.desc)
+
+    def run(self) -> None:
+        rc = self._fn(self._desc_ref, ctypes.c_void_p(self.ws.data_ptr()), self.ws.numel(), _stream())
+        _check(rc, "clsa_decode_step")
+
+
+def decode_step(layer_src, q, k_cache, v_cache, q_idx, k_idx, w, k, kv_len=None, scale=0.0):
+    """One clsa_decode_step call. Returns (outs, lses, idx_cache)."""
+    st = DecodeStep(layer_src, q, k_cache, v_cache, q_idx, k_idx, w, k, kv_len, scale)
+    st.run()
+    return st.out, st.lse, st.idx
+
+
+def block_union_build(idx: torch.Tensor, kv_len: int, block: int, Hkv: int):
+    """clsa_block_union_build. Returns (kv_indptr [B*Hkv+1], kv_indices [capacity]) int32."""
+    _dev(idx, "idx", (torch.int32,))
+    B, T, k = idx.shape
+    nblk = math.ceil(kv_len / block)
+    indptr = torch.empty(B * Hkv + 1, dtype=torch.int32, device=idx.device)
+    indices = torch.empty(max(1, B * Hkv * nblk), dtype=torch.int32, device=idx.device)
+    ws = _workspace(workspace_bytes(OP_BLOCK_UNION, B=B, T=1, kv_len=kv_len, block=block), idx.device)
+    rc = load().clsa_block_union_build(_ptr(idx), B, T, k, kv_len, block, Hkv, _ptr(indptr),
+                                       _ptr(indices), _ptr(ws), ws.numel(), _stream())
+    _check(rc, "clsa_block_union_build")
+    return indptr, indices
+
+
+def block_paged_attn(q, k_cache, v_cache, kv_indptr, kv_indices, block: int, kv_len: Optional[int] = None,
+                     scale: float = 0.0, out=None, lse=None, want_lse: bool = True):
+    """clsa_block_paged_attn. Returns (out, lse)."""
+    _dev(q, "q", (torch.bfloat16,))
+    B, T, Hq, D = q.shape
+    L_cap, Hkv = k_cache.shape[1], k_cache.shape[2]
+    _dev(k_cache, "k_cache", (q.dtype,), (B, L_cap, Hkv, D))
+    _dev(v_cache, "v_cache", (q.dtype,), (B, L_cap, Hkv, D))
+    _dev(kv_indptr, "kv_indptr", (torch.int32,), (B * Hkv + 1,))
+    _dev(kv_indices, "kv_indices", (torch.int32,))
+    kv_len = L_cap if kv_len is None else kv_len
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and want_lse:
+        lse = torch.empty((B, T, Hq), dtype=torch.float32, device=q.device)
+    rc = load().clsa_block_paged_attn(_ptr(q), _ptr(k_cache), _ptr(v_cache), _DT[q.dtype],
+                                      _ptr(kv_indptr), _ptr(kv_indices), block, _ptr(out), _ptr(lse),
+                                      B, T, Hq, Hkv, D, kv_len, L_cap, float(scale), _stream())
+    _check(rc, "clsa_block_paged_attn")
+    return out, lse

@@ -1,0 +1,225 @@
+// index_score.hip — indexer scores on gfx950 matrix cores.
+//
+// Computes, for every query (b, t) and visible cache position s,
+//   score = sum_h w[h] * max(0, q_idx[h, :] . k_idx[s, :])
+// (IndexCache summary, "1. Problématique": the lightning indexer scores every
+// previous token; CLSA article, "Comment CLSA fonctionne": the shared indexer
+// scores once). Positions a query does not see get -inf.
+//
+// Decode shape: per query the work is a [H_I x D_I] x [D_I x L] product whose
+// operand A (the query's indexer heads) is tiny and read once, while B (one
+// indexer key per cached token) streams from HBM exactly once. The kernel
+// keeps A in registers for the whole launch, feeds B straight from global
+// memory into MFMA operands (each key row is used by exactly one wave, so
+// staging it through LDS would only add a round trip), and folds the ReLU,
+// head weights and head sum into the epilogue so per-head scores never leave
+// registers.
+//
+// MFMA (v_mfma_f32_16x16x32_bf16 / _fp8_fp8, wave64): lane l supplies row
+// l%16 of A and column l%16 of B for the k-slice picked by l/16, and the
+// 16x16 result element (i, j) lands in lane j + 16*(i/4), slot i%4. The sum
+// runs over every k of the instruction, so the d-index carried by (lane
+// group, slot) is free as long as A and B agree: lane group g, k-step s,
+// slot e carries d = g*(D_I/4) + 8*s + e, which makes each lane's share of a
+// key row one contiguous run of D_I/4 elements.
+#include "kernels.h"
+
+namespace clsa {
+namespace {
+
+constexpr int kIdxThreads = 256;  // 4 waves
+constexpr int kKeysPerWaveIter = 64;  // 4 MFMA tiles of 16 keys
+
+template <int DT>
+struct IdxElem;
+template <>
+struct IdxElem<CLSA_BF16> {
+  static constexpr int bytes = 2;
+  typedef bf16x8 frag;  // 8 elements per lane per k-step
+  static __device__ __forceinline__ frag load(const uint8_t* p) {
+    return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(p));
+  }
+  static __device__ __forceinline__ f32x4 mfma(frag a, frag b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+};
+template <>
+struct IdxElem<CLSA_FP8_E4M3FN> {
+  static constexpr int bytes = 1;
+  typedef long frag;
+  static __device__ __forceinline__ frag load(const uint8_t* p) {
+    return *reinterpret_cast<const long*>(p);
+  }
+  static __device__ __forceinline__ f32x4 mfma(frag a, frag b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(a, b, c, 0, 0, 0);
+  }
+};
+
+// grid: (ceil(kv_len / keys_per_wg), B*T), block: 256.
+template <int DT, int DI, int HI>
+__global__ __launch_bounds__(kIdxThreads) void idx_score_mfma(
+    const uint8_t* __restrict__ q_idx, const uint8_t* __restrict__ k_idx,
+    const float* __restrict__ w, float* __restrict__ scores, int T, int kv_len, int L_cap,
+    int keys_per_wg) {
+  using E = IdxElem<DT>;
+  constexpr int NS = DI / 32;          // k-steps per key row
+  constexpr int NH = HI / 16;          // head tiles
+  constexpr int SPAN = DI / 4 * E::bytes;  // bytes of a key row per lane
+
+  const int lane = threadIdx.x % kWave;
+  const int wave = threadIdx.x / kWave;
+  const int col = lane % 16;   // A row / B column
+  const int grp = lane / 16;   // k-slice group
+  const int bt = blockIdx.y;
+  const int b = bt / T, t = bt % T;
+  const int vis = kv_len - T + t + 1;
+
+  // A fragments: this query's indexer heads, resident for the whole launch.
+  typename E::frag a[NH][NS];
+  const uint8_t* qrow = q_idx + (size_t)bt * HI * DI * E::bytes;
+#pragma unroll
+  for (int ht = 0; ht < NH; ht++)
+#pragma unroll
+    for (int s = 0; s < NS; s++)
+      a[ht][s] = E::load(qrow + ((size_t)(ht * 16 + col) * DI + grp * (DI / 4) + 8 * s) * E::bytes);
+  // Head weights for the 4 result slots this lane holds in each head tile.
+  float wv[NH][4];
+#pragma unroll
+  for (int ht = 0; ht < NH; ht++)
+#pragma unroll
+    for (int r = 0; r < 4; r++) wv[ht][r] = w[(size_t)bt * HI + ht * 16 + 4 * grp + r];
+
+  const uint8_t* kbase = k_idx + (size_t)b * L_cap * DI * E::bytes + grp * SPAN;
+  float* srow = scores + (size_t)bt * kv_len;
+  const int k0 = blockIdx.x * keys_per_wg;
+  const int k1 = min(k0 + keys_per_wg, kv_len);
+
+  for (int base = k0 + wave * kKeysPerWaveIter; base < k1; base += 4 * kKeysPerWaveIter) {
+    const int key_out = base + grp * 16 + col;  // key whose score this lane stores
+    if (base >= vis) {  // whole group past this query's visible range (wave-uniform)
+      if (key_out < k1) srow[key_out] = -INFINITY;
+      continue;
+    }
+    // B fragments for 4 tiles of 16 keys; rows past the visible range are
+    // clamped to a visible row and their results discarded.
+    typename E::frag bf[4][NS];
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      const int key = min(base + j * 16 + col, vis - 1);
+      const uint8_t* p = kbase + (size_t)key * DI * E::bytes;
+#pragma unroll
+      for (int s = 0; s < NS; s++) bf[j][s] = E::load(p + 8 * s * E::bytes);
+    }
+    float res = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      f32x4 acc[NH];
+#pragma unroll
+      for (int ht = 0; ht < NH; ht++) acc[ht] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < NS; s++)
+#pragma unroll
+        for (int ht = 0; ht < NH; ht++) acc[ht] = E::mfma(a[ht][s], bf[j][s], acc[ht]);
+      float v = 0.f;
+#pragma unroll
+      for (int ht = 0; ht < NH; ht++)
+#pragma unroll
+        for (int r = 0; r < 4; r++) v += wv[ht][r] * fmaxf(acc[ht][r], 0.f);
+      v += __shfl_xor(v, 16, kWave);
+      v += __shfl_xor(v, 32, kWave);
+      if (grp == j) res = v;
+    }
+    if (key_out < k1) srow[key_out] = key_out < vis ? res : -INFINITY;
+  }
+}
+
+// Float32 indexer (small head counts): one thread per key, the query's heads
+// and weights staged in LDS. grid: (ceil(kv_len/256), B*T), block 256,
+// dynamic LDS (H*D + H) floats.
+__global__ __launch_bounds__(256) void idx_score_f32(const float* __restrict__ q_idx,
+                                                     const float* __restrict__ k_idx,
+                                                     const float* __restrict__ w,
+                                                     float* __restrict__ scores, int T, int H,
+                                                     int D, int kv_len, int L_cap) {
+  extern __shared__ float sh[];
+  const int bt = blockIdx.y;
+  const int b = bt / T, t = bt % T;
+  const int vis = kv_len - T + t + 1;
+  for (int i = threadIdx.x; i < H * D; i += blockDim.x) sh[i] = q_idx[(size_t)bt * H * D + i];
+  for (int i = threadIdx.x; i < H; i += blockDim.x) sh[H * D + i] = w[(size_t)bt * H + i];
+  __syncthreads();
+  const int s = blockIdx.x * blockDim.x + threadIdx.x;
+  if (s >= kv_len) return;
+  float* out = scores + (size_t)bt * kv_len + s;
+  if (s >= vis) {
+    *out = -INFINITY;
+    return;
+  }
+  const float* kr = k_idx + ((size_t)b * L_cap + s) * D;
+  float total = 0.f;
+  for (int h = 0; h < H; h++) {
+    float dot = 0.f;
+    for (int d = 0; d < D; d++) dot = fmaf(sh[h * D + d], kr[d], dot);
+    total = fmaf(sh[H * D + h], fmaxf(dot, 0.f), total);
+  }
+  *out = total;
+}
+
+template <int DT, int DI, int HI>
+int launch_mfma(const void* q, const void* k, const float* w, float* scores, int B, int T,
+                int kv_len, int L_cap, hipStream_t stream) {
+  const int keys_per_wg = 1024;
+  dim3 grid((kv_len + keys_per_wg - 1) / keys_per_wg, B * T);
+  hipLaunchKernelGGL((idx_score_mfma<DT, DI, HI>), grid, dim3(kIdxThreads), 0, stream,
+                     static_cast<const uint8_t*>(q), static_cast<const uint8_t*>(k), w, scores, T,
+                     kv_len, L_cap, keys_per_wg);
+  return check_launch("idx_score_mfma");
+}
+
+template <int DT, int DI>
+int dispatch_heads(int H_I, const void* q, const void* k, const float* w, float* scores, int B,
+                   int T, int kv_len, int L_cap, hipStream_t stream) {
+  switch (H_I) {
+    case 16: return launch_mfma<DT, DI, 16>(q, k, w, scores, B, T, kv_len, L_cap, stream);
+    case 32: return launch_mfma<DT, DI, 32>(q, k, w, scores, B, T, kv_len, L_cap, stream);
+    case 48: return launch_mfma<DT, DI, 48>(q, k, w, scores, B, T, kv_len, L_cap, stream);
+    case 64: return launch_mfma<DT, DI, 64>(q, k, w, scores, B, T, kv_len, L_cap, stream);
+  }
+  return set_error(CLSA_ERR_UNSUPPORTED, "index_score: H_I=%d", H_I);
+}
+
+template <int DT>
+int dispatch_dim(int H_I, int D_I, const void* q, const void* k, const float* w, float* scores,
+                 int B, int T, int kv_len, int L_cap, hipStream_t stream) {
+  if (D_I == 64) return dispatch_heads<DT, 64>(H_I, q, k, w, scores, B, T, kv_len, L_cap, stream);
+  if (D_I == 128) return dispatch_heads<DT, 128>(H_I, q, k, w, scores, B, T, kv_len, L_cap, stream);
+  return set_error(CLSA_ERR_UNSUPPORTED, "index_score: D_I=%d", D_I);
+}
+
+}  // namespace
+
+bool index_score_supported(int idx_dtype, int H_I, int D_I) {
+  if (idx_dtype == CLSA_F32) return H_I >= 1 && D_I >= 1 && H_I * D_I <= 8192;
+  if (idx_dtype == CLSA_BF16 || idx_dtype == CLSA_FP8_E4M3FN)
+    return (H_I == 16 || H_I == 32 || H_I == 48 || H_I == 64) && (D_I == 64 || D_I == 128);
+  return false;
+}
+
+int launch_index_score(const void* q_idx, const void* k_idx, int idx_dtype, const float* w,
+                       float* scores, int B, int T, int H_I, int D_I, int kv_len, int L_cap,
+                       hipStream_t stream) {
+  if (idx_dtype == CLSA_F32) {
+    dim3 grid((kv_len + 255) / 256, B * T);
+    size_t lds = sizeof(float) * ((size_t)H_I * D_I + H_I);
+    hipLaunchKernelGGL(idx_score_f32, grid, dim3(256), lds, stream,
+                       static_cast<const float*>(q_idx), static_cast<const float*>(k_idx), w,
+                       scores, T, H_I, D_I, kv_len, L_cap);
+    return check_launch("idx_score_f32");
+  }
+  if (idx_dtype == CLSA_BF16)
+    return dispatch_dim<CLSA_BF16>(H_I, D_I, q_idx, k_idx, w, scores, B, T, kv_len, L_cap, stream);
+  return dispatch_dim<CLSA_FP8_E4M3FN>(H_I, D_I, q_idx, k_idx, w, scores, B, T, kv_len, L_cap,
+                                       stream);
+}
+
+}  // namespace clsa

@@ -1,0 +1,49 @@
+// kernels.h — internal launchers of libclsa (not part of the C ABI).
+// Every launcher assumes its arguments were validated by api.cpp and returns
+// a clsa_status.
+#pragma once
+
+#include "common.h"
+
+namespace clsa {
+
+// ---- indexer score ---------------------------------------------------------
+int launch_index_score(const void* q_idx, const void* k_idx, int idx_dtype, const float* w,
+                       float* scores, int B, int T, int H_I, int D_I, int kv_len, int L_cap,
+                       hipStream_t stream);
+bool index_score_supported(int idx_dtype, int H_I, int D_I);
+
+// ---- top-k -----------------------------------------------------------------
+// Buffers: hist [rows * kTopkBins] u32 (must be zero on entry; left zero),
+// counts [rows * nchunks] u32, cand [rows * nchunks * kTopkChunk] i32.
+constexpr int kTopkBins = 4096;
+constexpr int kTopkChunk = 4096;
+constexpr int kTopkMaxChunks = 1024;
+inline int topk_nchunks(int kv_len) { return (kv_len + kTopkChunk - 1) / kTopkChunk; }
+int launch_topk(const float* scores, int B, int T, int kv_len, int k, int32_t* idx,
+                uint32_t* hist, uint32_t* counts, int32_t* cand, hipStream_t stream);
+
+// ---- sparse attention --------------------------------------------------------
+// Buffers: counters [B*T*Hkv] u32 (must be zero on entry when splits > 1;
+// left zero), partials [B*T*Hq*splits*(D+2)] f32.
+struct AttnSplit {
+  int splits, rows_per_split;
+};
+AttnSplit attn_split(int B, int T, int Hkv, int k);
+bool sparse_attn_supported(int dtype, int Hq, int Hkv, int D);
+int launch_sparse_attn(const void* q, const void* kc, const void* vc, int dtype, const int32_t* idx,
+                       int k, void* out, float* lse, int B, int T, int Hq, int Hkv, int D,
+                       int kv_len, int L_cap, float scale, uint32_t* counters, float* partials,
+                       hipStream_t stream);
+
+// ---- block union comparator ----------------------------------------------------
+size_t block_union_ws_bytes(int B, int kv_len, int block);
+int launch_block_union(const int32_t* idx, int B, int T, int k, int kv_len, int block, int Hkv,
+                       int32_t* kv_indptr, int32_t* kv_indices, void* ws, hipStream_t stream);
+int launch_block_paged_attn(const void* q, const void* kc, const void* vc, int dtype,
+                            const int32_t* kv_indptr, const int32_t* kv_indices, int block,
+                            void* out, float* lse, int B, int T, int Hq, int Hkv, int D,
+                            int kv_len, int L_cap, float scale, hipStream_t stream);
+bool block_paged_attn_supported(int dtype, int Hq, int Hkv, int D, int block);
+
+}  // namespace clsa
