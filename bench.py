@@ -1,0 +1,226 @@
+#!/usr/bin/env python3
+"""Benchmark of the shared-index decode step on one MI355X.
+
+One step = one pass of the whole hot path over one batch: the indexer scores
+every cached key once, the top-k keeps k positions per query, and each of the
+N layers runs gathered sparse attention with that one index (CLSA: one
+indexer, N cross-decoder layers over one shared KV cache). Default workload:
+the 128K-context decode (B=4, kv_len=131072, 64x128 bf16 indexer, k=2048,
+16 layers, 32 q / 8 KV heads, dim 128, 1% needle keys), synthetic seeded
+inputs resident in HBM before the timed region starts.
+
+Prints one JSON line: tokens/s for the step, the attention kernel's
+achieved HBM GB/s against the 8 TB/s peak (HIP events recorded by the
+library around every attention launch inside the timed steps), and the CPU
+oracle timed on the host on a bounded sample of the same workload.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--config decode128k]
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import statistics
+import sys
+import time
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E
+
+
+def algorithmic_bytes(wl):
+    """Bytes each kernel of the step must move at least (its algorithmic traffic)."""
+    bt = wl.B * wl.T
+    e_kv = 2 if wl.dtype == 1 else 4
+    e_idx = {0: 4, 1: 2, 2: 1}[wl.idx_dtype]
+    vis_keys = sum(wl.kv_len - wl.T + t + 1 for t in range(wl.T)) * wl.B
+    index_score = (vis_keys * wl.D_I * e_idx + bt * wl.H_I * wl.D_I * e_idx + bt * wl.H_I * 4
+                   + bt * wl.kv_len * 4)
+    topk = bt * wl.kv_len * 4 + bt * wl.k * 4
+    attn = (bt * wl.k * wl.Hkv * wl.D * e_kv * 2      # gathered K and V rows
+            + bt * wl.k * 4                            # index
+            + 2 * bt * wl.Hq * wl.D * e_kv + bt * wl.Hq * 4)  # q, out, lse
+    return {"index_score": index_score, "topk": topk, "sparse_attn": attn}
+
+
+def cpu_baseline(wl, X, budget_s=12.0):
+    """The oracle's decode step (all layers, one indexer pass) on host copies of
+    the same inputs, single-threaded, one batch element per call, cycling over
+    the batch until the time budget is spent (at least one call)."""
+    import oracle
+    from token_sparse_attention_clsa_amd import inputs as inp
+
+    host = []
+    for b in range(wl.B):
+        memo = {}  # layers share one cache: copy each distinct tensor once
+
+        def sl(t):
+            if t is None:
+                return None
+            if id(t) not in memo:
+                memo[id(t)] = inp.raw(t[b:b + 1])
+            return memo[id(t)]
+
+        host.append(([sl(t) for t in X.q], [sl(t) for t in X.k_cache], [sl(t) for t in X.v_cache],
+                     [sl(t) for t in X.q_idx], [sl(t) for t in X.k_idx], [sl(t) for t in X.w]))
+    done, t_total = 0, 0.0
+    while done == 0 or t_total < budget_s:
+        q, kc, vc, qi, ki, w = host[done % wl.B]
+        t0 = time.perf_counter()
+        oracle.decode_step(wl.layer_src, q, kc, vc, wl.dtype, qi, ki, w, wl.idx_dtype, wl.kv_len, wl.k)
+        t_total += time.perf_counter() - t0
+        done += 1
+    return {
+        "value": done * wl.T / t_total,
+        "unit": "tokens/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"{done} single-batch-element decode steps ({wl.n_layers} layers, "
+                  f"{len(wl.f_layers)} indexer pass, kv_len {wl.kv_len}) of the same inputs, "
+                  f"{t_total:.1f} s of single-threaded CPU time",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", default="decode128k")
+    ap.add_argument("--variant", default="gauss", choices=["gauss", "int"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=12.0)
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}, WORLD_SIZE {world}); "
+              "the shared-index decode step is not sharded across GPUs in this build",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import token_sparse_attention_clsa_amd as clsa
+    from token_sparse_attention_clsa_amd import inputs as inp
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a HIP device", file=sys.stderr)
+        sys.exit(1)
+    clsa.load()
+    wl = inp.config(args.config)
+    print(f"[bench] workload {wl.name}: B={wl.B} T={wl.T} kv_len={wl.kv_len} layers={wl.n_layers} "
+          f"F={len(wl.f_layers)} k={wl.k}", file=sys.stderr, flush=True)
+    X = inp.make(wl, args.variant, seed=7, device="cuda")
+    n = wl.n_layers
+    K, W = args.steps, args.warmup
+    step = clsa.DecodeStep(wl.layer_src, X.q, X.k_cache, X.v_cache, X.q_idx, X.k_idx, X.w, wl.k,
+                           kv_len=wl.kv_len)
+    for _ in range(W):
+        step.run()
+    torch.cuda.synchronize()
+    print(f"[bench] warmup done ({W} steps)", file=sys.stderr, flush=True)
+
+    # Timed region: exactly K steps, nothing else enqueued between them.
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record()
+    for _ in range(K):
+        step.run()
+    e1.record()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_per_step = elapsed * 1e3 / K
+    ms_per_step_events = e0.elapsed_time(e1) / K
+    print(f"[bench] timed {K} steps: {ms_per_step * 1e3:.1f} us/step (events {ms_per_step_events * 1e3:.1f})",
+          file=sys.stderr, flush=True)
+
+    # Per-kernel averages: R back-to-back launches of one entry point on the
+    # stream, bracketed by one event pair (no event between launches, which
+    # would serialise the queue), same shapes and inputs as the step.
+    f0 = wl.f_layers[0]
+    R = max(4 * K, 64)
+    scores = torch.empty((wl.B, wl.T, wl.kv_len), dtype=torch.float32, device="cuda")
+    idx = step.idx
+    topk_ws = torch.empty(clsa.workspace_bytes(0, B=wl.B, T=wl.T, kv_len=wl.kv_len, k=wl.k),
+                          dtype=torch.uint8, device="cuda")
+    attn_ws = torch.empty(max(256, clsa.workspace_bytes(1, B=wl.B, T=wl.T, Hq=wl.Hq, Hkv=wl.Hkv, D=wl.D,
+                                                        k=wl.k)), dtype=torch.uint8, device="cuda")
+    out = [torch.empty_like(X.q[l]) for l in range(n)]
+    lse = [torch.empty((wl.B, wl.T, wl.Hq), dtype=torch.float32, device="cuda") for _ in range(n)]
+
+    def per_launch_us(fn):
+        for i in range(3):
+            fn(i)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record()
+        for i in range(R):
+            fn(i)
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) * 1e3 / R
+
+    us_index = per_launch_us(lambda i: clsa.index_score(X.q_idx[f0], X.k_idx[f0], X.w[f0], kv_len=wl.kv_len,
+                                                        out=scores))
+    us_topk = per_launch_us(lambda i: clsa.topk(scores, wl.k, out=idx, ws=topk_ws))
+    us_attn = per_launch_us(lambda i: clsa.sparse_attn(X.q[i % n], X.k_cache[i % n], X.v_cache[i % n], idx,
+                                                       kv_len=wl.kv_len, out=out[i % n], lse=lse[i % n],
+                                                       ws=attn_ws))
+    alg = algorithmic_bytes(wl)
+    attn_gbs = alg["sparse_attn"] / (us_attn * 1e-6) / 1e9
+    step_bytes = len(wl.f_layers) * (alg["index_score"] + alg["topk"]) + n * alg["sparse_attn"]
+    f_layers = wl.f_layers
+
+    tokens_per_step = wl.B * wl.T
+    result = {
+        "metric": "decode tokens/sec + achieved HBM GB/s, sparse-attn step @128K ctx, top-k 2048",
+        "value": tokens_per_step / (ms_per_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if wl.dtype == 1 else "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{wl.name}: decode B={wl.B}, kv_len={wl.kv_len}, indexer {wl.H_I}x{wl.D_I} "
+                        f"{inp.DTYPE_NAME[wl.idx_dtype]}, top-k {wl.k}, {n} layers sharing one index "
+                        f"({len(f_layers)} indexer pass), GQA {wl.Hq}q/{wl.Hkv}kv x {wl.D}",
+            "variant": args.variant,
+            "global_batch": wl.B,
+            "seq_len": wl.kv_len,
+            "parallelism": "single GPU",
+        },
+        "achieved_hbm_gbs_step": step_bytes / (ms_per_step * 1e-3) / 1e9,
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "sparse_attn (attn_split_kernel + attn_combine_kernel per call)",
+            "achieved": attn_gbs,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": attn_gbs / HBM_PEAK_GBS,
+            "traffic": None,
+            "bytes_per_launch": alg["sparse_attn"],
+            "avg_launch_us": us_attn,
+        },
+        "kernels_us": {
+            "sparse_attn": us_attn,
+            "index_score": us_index,
+            "topk": us_topk,
+            "index_score_gbs": alg["index_score"] / (us_index * 1e-6) / 1e9,
+        },
+        "ms_per_step_events": ms_per_step_events,
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (oracle) ...", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(wl, X, args.cpu_budget)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -76,7 +76,8 @@ def test_topk_rejects(lib):
     assert lib.clsa_topk(None, 1, 1, 100, 5, FAKE, FAKE, 1 << 20, None) == -1
     assert lib.clsa_topk(FAKE, 1, 1, 100, 5, FAKE, None, 0, None) == -3            # no workspace
     assert lib.clsa_topk(FAKE, 1, 1, 100, 5, FAKE, FAKE, 16, None) == -3           # too small
-    assert lib.clsa_topk(FAKE, 1, 1, 5_000_000, 5, FAKE, FAKE, 1 << 40, None) == -2
+    assert lib.clsa_topk(FAKE, 70000, 1, 100, 5, FAKE, FAKE, 1 << 40, None) == -2    # B*T above grid limit
+    assert lib.clsa_topk(FAKE, 1, 1, 5_000_000, 5, FAKE, FAKE, 1 << 40, None) == -2  # kv_len above 4M
 
 
 def test_sparse_attn_rejects(lib):

@@ -1,0 +1,119 @@
+"""GPU parity of clsa_decode_step (indexer -> top-k -> N attention layers
+sharing the index) against the oracle's decode step, on the shapes of each
+workload at sizes the oracle finishes in seconds.
+
+With the integer indexer recipe the index is unique, so the index cache
+left by the last F layer must match bit for bit and every layer's attention
+must match the float64 oracle (which attends with its own index) within the
+attention tolerance. With Gaussian indexer inputs the index may legitimately
+differ at near-ties; there the selection is checked against the oracle's
+scores and the float32 rounding bound.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import token_sparse_attention_clsa_amd as clsa
+from token_sparse_attention_clsa_amd import inputs as inp
+
+from gpu_util import DEV, TOL_LSE, TOL_OUT, announce, lse_close, max_abs, out_f64, raw, require_gpu
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    require_gpu()
+
+
+def _run(wl, variant, seed=1):
+    X = inp.make(wl, variant, seed=seed, device=DEV)
+    st = clsa.DecodeStep(wl.layer_src, X.q, X.k_cache, X.v_cache, X.q_idx, X.k_idx, X.w, wl.k,
+                         kv_len=wl.kv_len)
+    st.run()
+    torch.cuda.synchronize()
+    return X, st
+
+
+def _oracle(wl, X):
+    none_or_raw = lambda t: None if t is None else raw(t)
+    return oracle.decode_step(wl.layer_src, [raw(t) for t in X.q], [raw(t) for t in X.k_cache],
+                              [raw(t) for t in X.v_cache], wl.dtype, [none_or_raw(t) for t in X.q_idx],
+                              [none_or_raw(t) for t in X.k_idx], [none_or_raw(t) for t in X.w],
+                              wl.idx_dtype, wl.kv_len, wl.k)
+
+
+REDUCED = [
+    ("tiny", {}),
+    ("decode32k", dict(B=2, kv_len=8192)),
+    ("decode32k", dict(B=2, kv_len=6000, idx_dtype=inp.FP8_E4M3FN)),
+    ("decode128k", dict(B=1, kv_len=20000, layer_src=[0] * 5)),
+    ("indexcache48", dict(B=2, kv_len=4099, layer_src=[4 * (l // 4) for l in range(12)])),
+    ("prefill2k", dict(T=16, kv_len=3000, k=1024)),
+    ("decode32k", dict(B=1, kv_len=1500, k=2048, layer_src=[0, 0])),   # k above kv_len: padding
+]
+
+
+@pytest.mark.parametrize("name,over", REDUCED)
+def test_decode_step_integer_index_matches_oracle(name, over):
+    wl = inp.config(name, **over)
+    announce("decode_step int", name, over)
+    X, st = _run(wl, "int")
+    outs, lses, idx, calls = _oracle(wl, X)
+    assert calls == len(wl.f_layers)
+    assert np.array_equal(st.idx.cpu().numpy(), idx)
+    for l in range(wl.n_layers):
+        assert max_abs(out_f64(st.out[l]), outs[l]) <= TOL_OUT[wl.dtype], f"layer {l}"
+        lse_close(st.lse[l].cpu().numpy(), lses[l], TOL_LSE[wl.dtype])
+
+
+def test_decode_step_gaussian_selection_within_rounding_bound():
+    wl = inp.config("decode128k", B=2, kv_len=16384, layer_src=[0, 0, 0])
+    announce("decode_step gauss", wl.name, wl.B, wl.kv_len)
+    X, st = _run(wl, "gauss")
+    q_i, k_i, w = raw(X.q_idx[0]), raw(X.k_idx[0]), raw(X.w[0])
+    ref, bound = oracle.index_score(q_i, k_i, wl.idx_dtype, w, wl.kv_len, with_bound=True)
+    got = st.idx.cpu().numpy()
+    ref_idx = oracle.topk(ref, wl.k)
+    eps = 2.0 ** -16 * bound  # float32 rounding bound of each GPU score
+    for b in range(wl.B):
+        g, r = set(got[b, 0].tolist()), set(ref_idx[b, 0].tolist())
+        assert len(g) == wl.k
+        theta = ref[b, 0, ref_idx[b, 0]].min()
+        # a disagreement is allowed only where rounding can reorder a position
+        # against the threshold: |score - theta| <= eps(s) + max eps of the row
+        for s in g ^ r:
+            assert abs(ref[b, 0, s] - theta) <= eps[b, 0, s] + eps[b, 0].max(), s
+    # attention of every layer, against the oracle fed the GPU's index
+    for l in range(wl.n_layers):
+        o, ls = oracle.sparse_attn(raw(X.q[l]), raw(X.k_cache[l]), raw(X.v_cache[l]), wl.dtype, got, wl.kv_len)
+        assert max_abs(out_f64(st.out[l]), o) <= TOL_OUT[wl.dtype]
+        lse_close(st.lse[l].cpu().numpy(), ls, TOL_LSE[wl.dtype])
+
+
+def test_decode_step_shared_layers_with_same_query_agree_bitwise():
+    wl = inp.config("decode32k", B=2, kv_len=5000, layer_src=[0, 0, 0])
+    announce("decode_step same-q layers")
+    X = inp.make(wl, "gauss", seed=3, device=DEV)
+    q = [X.q[0]] * 3
+    st = clsa.DecodeStep(wl.layer_src, q, X.k_cache, X.v_cache, X.q_idx, X.k_idx, X.w, wl.k)
+    st.run()
+    torch.cuda.synchronize()
+    assert torch.equal(st.out[0], st.out[1]) and torch.equal(st.out[0], st.out[2])
+
+
+def test_decode_step_events_record_every_stage():
+    wl = inp.config("decode32k", B=2, kv_len=4096, layer_src=[0, 0, 2, 2])
+    announce("decode_step events")
+    X = inp.make(wl, "gauss", seed=4, device=DEV)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4 * wl.n_layers)]
+    st = clsa.DecodeStep(wl.layer_src, X.q, X.k_cache, X.v_cache, X.q_idx, X.k_idx, X.w, wl.k, events=ev)
+    st.run()
+    torch.cuda.synchronize()
+    for l in range(wl.n_layers):
+        assert ev[4 * l + 2].elapsed_time(ev[4 * l + 3]) > 0          # attention ran
+        if wl.layer_src[l] == l:
+            assert ev[4 * l].elapsed_time(ev[4 * l + 1]) > 0          # indexer ran
+            assert ev[4 * l + 1].elapsed_time(ev[4 * l + 2]) > 0      # top-k ran

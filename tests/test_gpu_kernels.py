@@ -94,9 +94,12 @@ TOPK_CASES = [
     ("gauss", 1, 1, 1000, 1),
     ("gauss", 1, 1, 1000, 1000),       # k == visible
     ("gauss", 2, 1, 700, 2048),        # k > visible: -1 padding
-    ("gauss", 1, 6, 5000, 4990),       # causal rows, some with fewer than k visible
+    ("gauss", 1, 6, 5000, 4997),       # causal rows: 2 with fewer than k visible, 1 with exactly k
     ("ties", 1, 64, 8192, 512),        # many causal rows
     ("gauss", 1, 1, 4097, 4096),
+    ("strided", 1, 1, 131072, 3000),   # a strided sample sees only the high positions: full-row redo
+    ("strided", 2, 1, 131072, 1000),
+    ("needle", 2, 1, 131073, 2048),    # misaligned second row
 ]
 
 

@@ -39,50 +39,43 @@ struct Carver {
 };
 
 struct TopkWs {
-  size_t hist, counts, cand, total;
+  size_t counts, cand, spill, total;
 };
 TopkWs topk_ws(int rows, int kv_len) {
+  const TopkBuffers tb = topk_buffers(rows, kv_len);
   Carver c;
   TopkWs w;
-  const int nch = topk_nchunks(kv_len);
-  w.hist = c.add((size_t)rows * kTopkBins * 4);
-  w.counts = c.add((size_t)rows * nch * 4);
-  w.cand = c.add((size_t)rows * nch * kTopkChunk * 4);
+  w.counts = c.add(tb.counts_words * 4);
+  w.cand = c.add(tb.cand_words * 4);
+  w.spill = c.add(tb.spill_words * 4);
   w.total = c.off;
   return w;
 }
 
 struct AttnWs {
-  size_t counters, partials, total;
+  size_t partials, total;
 };
-AttnWs attn_ws(int B, int T, int Hq, int Hkv, int D, int k) {
+AttnWs attn_ws(int B, int T, int Hq, int Hkv, int k) {
   Carver c;
   AttnWs w;
-  const AttnSplit s = attn_split(B, T, Hkv, k);
-  w.counters = c.add((size_t)B * T * Hkv * 4);
-  w.partials = c.add(s.splits > 1 ? (size_t)B * T * Hq * s.splits * (D + 2) * 4 : 0);
+  w.partials = c.add(attn_partial_floats(B, T, Hq, Hkv, k) * 4);
   w.total = c.off;
   return w;
 }
 
-// Decode step: [hist | counters] first (cleared together once per step).
+// Decode step workspace: top-k buffers, attention split states, indexer
+// scores.
 struct StepWs {
-  size_t hist, counters, zero_bytes, counts, cand, partials, scores, total;
+  TopkWs topk;
+  size_t partials, scores, total;
 };
-StepWs step_ws(int B, int T, int Hq, int Hkv, int D, int kv_len, int k) {
-  const int rows = B * T;
-  const int nch = topk_nchunks(kv_len);
-  const AttnSplit s = attn_split(B, T, Hkv, k);
+StepWs step_ws(int B, int T, int Hq, int Hkv, int kv_len, int k) {
   StepWs w;
+  w.topk = topk_ws(B * T, kv_len);
   Carver c;
-  w.hist = c.add((size_t)rows * kTopkBins * 4);
-  w.counters = c.off;  // directly after the histogram (no padding needed: u32)
-  c.off = align_up(c.off + (size_t)rows * Hkv * 4, 256);
-  w.zero_bytes = w.counters + (size_t)rows * Hkv * 4;
-  w.counts = c.add((size_t)rows * nch * 4);
-  w.cand = c.add((size_t)rows * nch * kTopkChunk * 4);
-  w.partials = c.add(s.splits > 1 ? (size_t)rows * Hq * s.splits * (D + 2) * 4 : 0);
-  w.scores = c.add((size_t)rows * kv_len * 4);
+  c.off = w.topk.total;
+  w.partials = c.add(attn_partial_floats(B, T, Hq, Hkv, k) * 4);
+  w.scores = c.add((size_t)B * T * kv_len * 4);
   w.total = c.off;
   return w;
 }
@@ -120,7 +113,7 @@ int check_topk_args(const float* scores, int B, int T, int kv_len, int k, const 
   int rc = check_shape(B, T, kv_len, kv_len);
   if (rc) return rc;
   if (k < 1) return set_error(CLSA_ERR_INVALID_ARG, "topk: k=%d must be >= 1", k);
-  if (topk_nchunks(kv_len) > kTopkMaxChunks)
+  if (topk_buffers(1, kv_len).nchunks > kTopkMaxChunks)
     return set_error(CLSA_ERR_UNSUPPORTED, "topk: kv_len=%d above %d", kv_len,
                      kTopkMaxChunks * kTopkChunk);
   if (!aligned(scores, 4) || !aligned(idx, 4))
@@ -187,7 +180,7 @@ size_t clsa_workspace_bytes(int op, int B, int T, int Hq, int Hkv, int D, int kv
       return topk_ws(B * T, kv_len).total;
     case CLSA_OP_SPARSE_ATTN:
       if (Hq < 1 || Hkv < 1 || D < 1 || k < 1 || Hq % Hkv) return 0;
-      return attn_ws(B, T, Hq, Hkv, D, k).total;
+      return attn_ws(B, T, Hq, Hkv, k).total;
     case CLSA_OP_BLOCK_UNION:
       if (kv_len < 1 || block < 1) return 0;
       return block_union_ws_bytes(B, kv_len, block);
@@ -213,11 +206,9 @@ int clsa_topk(const float* scores, int B, int T, int kv_len, int k, int32_t* idx
     return set_error(CLSA_ERR_WORKSPACE, "topk: workspace of %zu bytes (256-aligned) required, got %zu",
                      L.total, ws ? ws_bytes : (size_t)0);
   char* base = static_cast<char*>(ws);
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  uint32_t* hist = reinterpret_cast<uint32_t*>(base + L.hist);
-  if ((rc = zero_words(hist, (size_t)B * T * kTopkBins, s))) return rc;
-  return launch_topk(scores, B, T, kv_len, k, idx, hist, reinterpret_cast<uint32_t*>(base + L.counts),
-                     reinterpret_cast<int32_t*>(base + L.cand), s);
+  return launch_topk(scores, B, T, kv_len, k, idx, reinterpret_cast<uint32_t*>(base + L.counts),
+                     reinterpret_cast<int32_t*>(base + L.cand),
+                     reinterpret_cast<int32_t*>(base + L.spill), static_cast<hipStream_t>(stream));
 }
 
 int clsa_sparse_attn(const void* q, const void* k_cache, const void* v_cache, int dtype,
@@ -229,18 +220,15 @@ int clsa_sparse_attn(const void* q, const void* k_cache, const void* v_cache, in
   if (rc) return rc;
   if (!(scale == scale) || isinf(scale))
     return set_error(CLSA_ERR_INVALID_ARG, "sparse_attn: scale must be finite");
-  const AttnWs L = attn_ws(B, T, Hq, Hkv, D, k);
+  const AttnWs L = attn_ws(B, T, Hq, Hkv, k);
   if (!ws || ws_bytes < L.total || !aligned(ws, 256))
     return set_error(CLSA_ERR_WORKSPACE,
                      "sparse_attn: workspace of %zu bytes (256-aligned) required, got %zu", L.total,
                      ws ? ws_bytes : (size_t)0);
   char* base = static_cast<char*>(ws);
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  uint32_t* counters = reinterpret_cast<uint32_t*>(base + L.counters);
-  if (attn_split(B, T, Hkv, k).splits > 1 && (rc = zero_words(counters, (size_t)B * T * Hkv, s)))
-    return rc;
   return launch_sparse_attn(q, k_cache, v_cache, dtype, idx, k, out, lse, B, T, Hq, Hkv, D, kv_len,
-                            L_cap, scale, counters, reinterpret_cast<float*>(base + L.partials), s);
+                            L_cap, scale, reinterpret_cast<float*>(base + L.partials),
+                            static_cast<hipStream_t>(stream));
 }
 
 static int check_step(const clsa_step_desc* d) {
@@ -286,28 +274,24 @@ static int check_step(const clsa_step_desc* d) {
 
 size_t clsa_decode_step_workspace_bytes(const clsa_step_desc* d) {
   if (check_step(d)) return 0;
-  return step_ws(d->B, d->T, d->Hq, d->Hkv, d->D, d->kv_len, d->k).total;
+  return step_ws(d->B, d->T, d->Hq, d->Hkv, d->kv_len, d->k).total;
 }
 
 int clsa_decode_step(const clsa_step_desc* d, void* ws, size_t ws_bytes, void* stream) {
   int rc = check_step(d);
   if (rc) return rc;
-  const StepWs L = step_ws(d->B, d->T, d->Hq, d->Hkv, d->D, d->kv_len, d->k);
+  const StepWs L = step_ws(d->B, d->T, d->Hq, d->Hkv, d->kv_len, d->k);
   if (!ws || ws_bytes < L.total || !aligned(ws, 256))
     return set_error(CLSA_ERR_WORKSPACE,
                      "decode_step: workspace of %zu bytes (256-aligned) required, got %zu", L.total,
                      ws ? ws_bytes : (size_t)0);
   hipStream_t s = static_cast<hipStream_t>(stream);
   char* base = static_cast<char*>(ws);
-  uint32_t* hist = reinterpret_cast<uint32_t*>(base + L.hist);
-  uint32_t* counters = reinterpret_cast<uint32_t*>(base + L.counters);
-  uint32_t* counts = reinterpret_cast<uint32_t*>(base + L.counts);
-  int32_t* cand = reinterpret_cast<int32_t*>(base + L.cand);
+  uint32_t* counts = reinterpret_cast<uint32_t*>(base + L.topk.counts);
+  int32_t* cand = reinterpret_cast<int32_t*>(base + L.topk.cand);
+  int32_t* spill = reinterpret_cast<int32_t*>(base + L.topk.spill);
   float* partials = reinterpret_cast<float*>(base + L.partials);
   float* scores = reinterpret_cast<float*>(base + L.scores);
-  // One clear per step: both the top-k histogram and the attention tickets
-  // are left zero by the kernels that use them, so later layers reuse them.
-  if ((rc = zero_words(hist, L.zero_bytes / 4, s))) return rc;
   for (int l = 0; l < d->n_layers; l++) {
     if ((rc = record(d->events, 4 * l, s))) return rc;
     if (d->layer_src[l] == l) {
@@ -315,7 +299,7 @@ int clsa_decode_step(const clsa_step_desc* d, void* ws, size_t ws_bytes, void* s
                               d->H_I, d->D_I, d->kv_len, d->L_cap, s);
       if (rc) return rc;
       if ((rc = record(d->events, 4 * l + 1, s))) return rc;
-      rc = launch_topk(scores, d->B, d->T, d->kv_len, d->k, d->idx_out, hist, counts, cand, s);
+      rc = launch_topk(scores, d->B, d->T, d->kv_len, d->k, d->idx_out, counts, cand, spill, s);
       if (rc) return rc;
     } else if ((rc = record(d->events, 4 * l + 1, s))) {
       return rc;
@@ -323,7 +307,7 @@ int clsa_decode_step(const clsa_step_desc* d, void* ws, size_t ws_bytes, void* s
     if ((rc = record(d->events, 4 * l + 2, s))) return rc;
     rc = launch_sparse_attn(d->q[l], d->k_cache[l], d->v_cache[l], d->dtype, d->idx_out, d->k,
                             d->out[l], d->lse ? d->lse[l] : nullptr, d->B, d->T, d->Hq, d->Hkv,
-                            d->D, d->kv_len, d->L_cap, d->scale, counters, partials, s);
+                            d->D, d->kv_len, d->L_cap, d->scale, partials, s);
     if (rc) return rc;
     if ((rc = record(d->events, 4 * l + 3, s))) return rc;
   }

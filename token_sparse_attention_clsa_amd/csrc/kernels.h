@@ -14,27 +14,31 @@ int launch_index_score(const void* q_idx, const void* k_idx, int idx_dtype, cons
 bool index_score_supported(int idx_dtype, int H_I, int D_I);
 
 // ---- top-k -----------------------------------------------------------------
-// Buffers: hist [rows * kTopkBins] u32 (must be zero on entry; left zero),
-// counts [rows * nchunks] u32, cand [rows * nchunks * kTopkChunk] i32.
+// Buffers: counts [rows * nchunks] u32, cand [rows * nchunks * kTopkChunk] i32,
+// spill [rows * kv_len] i32 (used only when a row is redone in full).
 constexpr int kTopkBins = 4096;
 constexpr int kTopkChunk = 4096;
-constexpr int kTopkMaxChunks = 1024;
-inline int topk_nchunks(int kv_len) { return (kv_len + kTopkChunk - 1) / kTopkChunk; }
+constexpr int kTopkMaxChunks = 1024;  // kv_len <= 4M
+struct TopkBuffers {
+  int nchunks;
+  size_t counts_words, cand_words, spill_words;
+};
+TopkBuffers topk_buffers(int rows, int kv_len);
 int launch_topk(const float* scores, int B, int T, int kv_len, int k, int32_t* idx,
-                uint32_t* hist, uint32_t* counts, int32_t* cand, hipStream_t stream);
+                uint32_t* counts, int32_t* cand, int32_t* spill, hipStream_t stream);
 
 // ---- sparse attention --------------------------------------------------------
-// Buffers: counters [B*T*Hkv] u32 (must be zero on entry when splits > 1;
-// left zero), partials [B*T*Hq*splits*(D+2)] f32.
+// Buffer: partials [attn_partial_floats(...)] f32 (split states; unused when
+// the k entries are not split).
 struct AttnSplit {
   int splits, rows_per_split;
 };
 AttnSplit attn_split(int B, int T, int Hkv, int k);
+size_t attn_partial_floats(int B, int T, int Hq, int Hkv, int k);
 bool sparse_attn_supported(int dtype, int Hq, int Hkv, int D);
 int launch_sparse_attn(const void* q, const void* kc, const void* vc, int dtype, const int32_t* idx,
                        int k, void* out, float* lse, int B, int T, int Hq, int Hkv, int D,
-                       int kv_len, int L_cap, float scale, uint32_t* counters, float* partials,
-                       hipStream_t stream);
+                       int kv_len, int L_cap, float scale, float* partials, hipStream_t stream);
 
 // ---- block union comparator ----------------------------------------------------
 size_t block_union_ws_bytes(int B, int kv_len, int block);

@@ -7,25 +7,32 @@
 // selected tokens; CLSA article, "Comment CLSA fonctionne": every layer
 // reuses the one index).
 //
-// Work split: one workgroup per (query, KV head, split of the k entries).
-// The G query heads of a KV head share every gathered row, so each row is
-// read from HBM once per layer. A row of one KV head is D contiguous
-// elements (token-major cache), gathered by 16 lanes with one 16-byte load
-// each (bf16), four rows per wave instruction. Scores use v_dot2_f32_bf16
-// on bf16 pairs and a 16-lane butterfly; softmax runs online in the log2
-// domain, in float32, one rescale per 4-row step. Lane groups and waves are
-// merged through shuffles and LDS; the splits of a (query, KV head) are
-// merged by whichever workgroup finishes last (an atomic ticket), reading
-// the partial states in split order so the result does not depend on
-// scheduling. The ticket is returned to zero by that workgroup.
+// Work split (index path): one workgroup per (query, split of the k
+// entries, block of KV heads), one wave per KV head. The split's index
+// entries are staged once in LDS and shared by the waves, so the waves of a
+// workgroup read the same tokens' K/V rows (contiguous across KV heads in the
+// token-major cache) at about the same time. A row of one KV head is D
+// contiguous elements, gathered by 16 lanes with one 16-byte load each
+// (bf16), four rows per wave instruction; each lane group keeps 8 rows of K
+// and V in flight before computing. Scores use v_dot2_f32_bf16 on bf16 pairs
+// and a 16-lane DPP butterfly; softmax runs online in the log2 domain in
+// float32 with one rescale per 8-row step; the G query heads of a KV head
+// share every gathered row, so each row leaves HBM once per layer.
+// With several splits, each split writes its (max, sum, unnormalised
+// output) state and a second small kernel merges the states of a head in
+// split order (deterministic). Merging inside the first kernel would need an
+// agent-scope release per workgroup, which on this GPU writes back the whole
+// L2 and costs more than the extra launch.
 #include "kernels.h"
 
 namespace clsa {
 namespace {
 
-constexpr int kAttnThreads = 256;  // 4 waves
 constexpr int kD = 128;
-constexpr int kRowsPerStep = 64;   // 4 waves x 4 lane groups x 4 rows
+constexpr int kTileRows = 512;        // index entries staged in LDS per tile
+constexpr int kMaxWaves = 8;          // KV heads per workgroup
+constexpr int kPart = kD + 4;         // split state record: m, l, pad, pad, o[128]
+constexpr int kMaxSplits = 2 * kD;    // the combine kernel reads <= 2 states per thread
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
@@ -36,6 +43,7 @@ struct AttnElem;
 template <>
 struct AttnElem<CLSA_BF16> {
   static constexpr int bytes = 2;
+  static constexpr int rows_per_step = 8;  // rows per lane group kept in flight
   struct Frag {
     uint4 u;  // 8 bf16
   };
@@ -63,10 +71,20 @@ struct AttnElem<CLSA_BF16> {
   static __device__ __forceinline__ void store(void* out, size_t i, float x) {
     static_cast<uint16_t*>(out)[i] = (uint16_t)f32_to_bf16_rne(x);
   }
+  // 8 consecutive outputs starting at element i (16-byte aligned).
+  static __device__ __forceinline__ void store8(void* out, size_t i, const float* x) {
+    uint4 u;
+    u.x = f32_to_bf16_rne(x[0]) | (f32_to_bf16_rne(x[1]) << 16);
+    u.y = f32_to_bf16_rne(x[2]) | (f32_to_bf16_rne(x[3]) << 16);
+    u.z = f32_to_bf16_rne(x[4]) | (f32_to_bf16_rne(x[5]) << 16);
+    u.w = f32_to_bf16_rne(x[6]) | (f32_to_bf16_rne(x[7]) << 16);
+    *reinterpret_cast<uint4*>(static_cast<uint16_t*>(out) + i) = u;
+  }
 };
 template <>
 struct AttnElem<CLSA_F32> {
   static constexpr int bytes = 4;
+  static constexpr int rows_per_step = 4;
   struct Frag {
     float4 a, b;  // 8 floats
   };
@@ -88,9 +106,24 @@ struct AttnElem<CLSA_F32> {
   static __device__ __forceinline__ void store(void* out, size_t i, float x) {
     static_cast<float*>(out)[i] = x;
   }
+  static __device__ __forceinline__ void store8(void* out, size_t i, const float* x) {
+    float4* o = reinterpret_cast<float4*>(static_cast<float*>(out) + i);
+    o[0] = make_float4(x[0], x[1], x[2], x[3]);
+    o[1] = make_float4(x[4], x[5], x[6], x[7]);
+  }
 };
 
-__device__ __forceinline__ float sum16(float v) {
+// Sum over each row of 16 lanes, result in all 16 lanes (DPP butterfly:
+// swap neighbours, swap pairs, mirror within 8, mirror within 16).
+__device__ __forceinline__ float dpp_sum16(float v) {
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false));
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, false));
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x140, 0xF, 0xF, false));
+  return v;
+}
+
+__device__ __forceinline__ float sum16_shfl(float v) {
   v += __shfl_xor(v, 1, kWave);
   v += __shfl_xor(v, 2, kWave);
   v += __shfl_xor(v, 4, kWave);
@@ -103,126 +136,51 @@ __device__ __forceinline__ float rescale(float a, float b) {
   return b == -INFINITY ? 1.f : exp2f(a - b);
 }
 
-// Where the attended positions come from.
-// IdxSrc: the k entries of the query's index row.
-struct IdxSrc {
-  const int32_t* idx;
-  int k;
-  const int32_t* row;
-  __device__ void bind(int bt, int g) { row = idx + (size_t)bt * k; }
-  __device__ int count() const { return k; }
-  __device__ int pos(int r) const { return row[r]; }
-};
-// BlockSrc: every position of the blocks listed for (b, g) in a block table
-// (kv_indptr / kv_indices), in table order.
-struct BlockSrc {
-  const int32_t* indptr;
-  const int32_t* indices;
-  int block, T, Hkv;
-  const int32_t* list;
-  int n;
-  __device__ void bind(int bt, int g) {
-    const int u = (bt / T) * Hkv + g;
-    list = indices + indptr[u];
-    n = (indptr[u + 1] - indptr[u]) * block;
-  }
-  __device__ int count() const { return n; }
-  __device__ int pos(int r) const { return list[r / block] * block + r % block; }
-};
-
-// grid (S, Hkv, B*T), block 256.
-template <int DT, int G, class Src>
-__global__ __launch_bounds__(kAttnThreads) void sparse_attn_kernel(
-    const char* __restrict__ q, const char* __restrict__ kc, const char* __restrict__ vc,
-    Src src, void* __restrict__ out, float* __restrict__ lse,
-    int T, int Hkv, int kv_len, int L_cap, float c_log2, int rows_per_split,
-    uint32_t* __restrict__ counters, float* __restrict__ partials) {
-  using E = AttnElem<DT>;
-  constexpr int ROW = kD * E::bytes;  // bytes of one KV head of one token
-  const int lane = threadIdx.x % kWave;
-  const int wave = threadIdx.x / kWave;
-  const int sub = lane % 16;   // element slice [8*sub, 8*sub + 8)
-  const int rg = lane / 16;    // row group within the wave
-  const int split = blockIdx.x, S = gridDim.x;
-  const int g = blockIdx.y;
-  const int bt = blockIdx.z;
-  const int b = bt / T, t = bt % T;
-  const int vis = kv_len - T + t + 1;
-  const int Hq = Hkv * G;
-
-  // This lane's slice of the G query heads.
-  typename E::Frag qf[G];
-#pragma unroll
-  for (int h = 0; h < G; h++)
-    qf[h] = E::load(q + (((size_t)bt * Hq + g * G + h) * kD + 8 * sub) * E::bytes);
-
+// Per-lane online-softmax state for the G query heads of one KV head, over
+// the 8-element slice of D this lane owns.
+template <int G>
+struct HeadState {
   float m[G], l[G], o[G][8];
-#pragma unroll
-  for (int h = 0; h < G; h++) {
-    m[h] = -INFINITY;
-    l[h] = 0.f;
-#pragma unroll
-    for (int e = 0; e < 8; e++) o[h][e] = 0.f;
-  }
-
-  src.bind(bt, g);
-  const char* kb = kc + ((size_t)b * L_cap * Hkv + g) * ROW + 8 * sub * E::bytes;
-  const char* vb = vc + ((size_t)b * L_cap * Hkv + g) * ROW + 8 * sub * E::bytes;
-  const size_t tok = (size_t)Hkv * ROW;  // bytes between consecutive tokens
-  const int r0 = split * rows_per_split;
-  const int r1 = min(src.count(), r0 + rows_per_split);
-
-  // wb is wave-uniform; lane group rg takes rows wb + 4*rg .. wb + 4*rg + 3.
-  for (int wb = r0 + wave * 16; wb < r1; wb += kRowsPerStep) {
-    const int base = wb + rg * 4;
-    int pos[4];
-    bool valid[4];
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-      const int r = base + i;
-      const int p = r < r1 ? src.pos(r) : -1;
-      valid[i] = p >= 0 && p < vis;
-      pos[i] = valid[i] ? p : 0;
-    }
-    typename E::Frag kf[4], vf[4];
-#pragma unroll
-    for (int i = 0; i < 4; i++) kf[i] = E::load(kb + (size_t)pos[i] * tok);
-#pragma unroll
-    for (int i = 0; i < 4; i++) vf[i] = E::load(vb + (size_t)pos[i] * tok);
-    float u[4][G];
-#pragma unroll
-    for (int i = 0; i < 4; i++)
-#pragma unroll
-      for (int h = 0; h < G; h++) {
-        const float s = sum16(E::dot(qf[h], kf[i]));
-        u[i][h] = valid[i] ? s * c_log2 : -INFINITY;
-      }
-    float v[4][8];
-#pragma unroll
-    for (int i = 0; i < 4; i++) E::to_f32(vf[i], v[i]);
+  __device__ void init() {
 #pragma unroll
     for (int h = 0; h < G; h++) {
-      const float mc = fmaxf(fmaxf(u[0][h], u[1][h]), fmaxf(u[2][h], u[3][h]));
+      m[h] = -INFINITY;
+      l[h] = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; e++) o[h][e] = 0.f;
+    }
+  }
+  // Fold in R rows: u[i][h] are log2-domain logits (-inf for skipped rows),
+  // v[i] the rows' value slices.
+  template <int R>
+  __device__ void update(const float (&u)[R][G], const float (&v)[R][8]) {
+#pragma unroll
+    for (int h = 0; h < G; h++) {
+      float mc = u[0][h];
+#pragma unroll
+      for (int i = 1; i < R; i++) mc = fmaxf(mc, u[i][h]);
       const float mn = fmaxf(m[h], mc);
       const float a = rescale(m[h], mn);
-      float p[4];
+      float p[R];
+      float ps = 0.f;
 #pragma unroll
-      for (int i = 0; i < 4; i++) p[i] = valid[i] ? exp2f(u[i][h] - mn) : 0.f;
-      l[h] = l[h] * a + (p[0] + p[1]) + (p[2] + p[3]);
+      for (int i = 0; i < R; i++) {
+        p[i] = u[i][h] == -INFINITY ? 0.f : exp2f(u[i][h] - mn);
+        ps += p[i];
+      }
+      l[h] = l[h] * a + ps;
 #pragma unroll
       for (int e = 0; e < 8; e++) {
         float x = o[h][e] * a;
 #pragma unroll
-        for (int i = 0; i < 4; i++) x = fmaf(p[i], v[i][e], x);
+        for (int i = 0; i < R; i++) x = fmaf(p[i], v[i][e], x);
         o[h][e] = x;
       }
       m[h] = mn;
     }
   }
-
-  // Merge the 4 row groups of the wave (lanes sub, sub+16, sub+32, sub+48).
-#pragma unroll
-  for (int x = 16; x <= 32; x <<= 1) {
+  // Merge with the state held by lane (lane ^ x).
+  __device__ void merge_xor(int x) {
 #pragma unroll
     for (int h = 0; h < G; h++) {
       const float m2 = __shfl_xor(m[h], x, kWave);
@@ -238,100 +196,303 @@ __global__ __launch_bounds__(kAttnThreads) void sparse_attn_kernel(
       m[h] = mn;
     }
   }
+};
 
-  // Merge the 4 waves through LDS: st[wave][h] = {m, l, o[128]}.
-  __shared__ float st[4][G][kD + 2];
-  __shared__ int s_last;
+// Split kernel of the index path.
+// grid (S, B*T, Hkv / NW), block 64 * NW; wave w handles KV head
+// g = blockIdx.z * NW + w over entries [split*rows, split*rows + rows) of the
+// query's index row. With S == 1 it writes out/lse, otherwise one state
+// record per (query, head, split).
+template <int DT, int G>
+__global__ __launch_bounds__(kWave * kMaxWaves) void attn_split_kernel(
+    const char* __restrict__ q, const char* __restrict__ kc, const char* __restrict__ vc,
+    const int32_t* __restrict__ idx, int k, void* __restrict__ out, float* __restrict__ lse,
+    int T, int Hkv, int kv_len, int L_cap, float c_log2, int rows_per_split,
+    float* __restrict__ partials) {
+  using E = AttnElem<DT>;
+  constexpr int RPI = G <= 4 ? E::rows_per_step : 4;  // fewer rows in flight for 8 heads
+  constexpr int ROW = kD * E::bytes;
+  __shared__ int s_pos[kTileRows];
+  const int lane = threadIdx.x % kWave;
+  const int wave = threadIdx.x / kWave;
+  const int nw = blockDim.x / kWave;
+  const int sub = lane % 16;  // element slice [8*sub, 8*sub + 8)
+  const int rg = lane / 16;   // lane group: its own rows
+  const int split = blockIdx.x, S = gridDim.x;
+  const int bt = blockIdx.y;
+  const int g = blockIdx.z * nw + wave;
+  const int b = bt / T, t = bt % T;
+  const int vis = kv_len - T + t + 1;
+  const int Hq = Hkv * G;
+  const int r0 = split * rows_per_split;
+  const int r1 = min(k, r0 + rows_per_split);
+  const int32_t* irow = idx + (size_t)bt * k;
+
+  typename E::Frag qf[G];
+#pragma unroll
+  for (int h = 0; h < G; h++)
+    qf[h] = E::load(q + (((size_t)bt * Hq + g * G + h) * kD + 8 * sub) * E::bytes);
+  HeadState<G> st;
+  st.init();
+
+  const char* kb = kc + ((size_t)b * L_cap * Hkv + g) * ROW + 8 * sub * E::bytes;
+  const char* vb = vc + ((size_t)b * L_cap * Hkv + g) * ROW + 8 * sub * E::bytes;
+  const size_t tok = (size_t)Hkv * ROW;  // bytes between consecutive tokens
+
+  for (int t0 = r0; t0 < r1; t0 += kTileRows) {  // uniform over the workgroup
+    const int n = min(kTileRows, r1 - t0);
+    __syncthreads();  // the previous tile's positions are no longer read
+    for (int i = threadIdx.x; i < n; i += blockDim.x) {
+      const int p = irow[t0 + i];
+      s_pos[i] = (p >= 0 && p < vis) ? p : -1;
+    }
+    __syncthreads();
+    for (int base = 0; base < n; base += 4 * RPI) {  // uniform over the wave
+      int pos[RPI];
+#pragma unroll
+      for (int i = 0; i < RPI; i++) {
+        const int r = base + rg * RPI + i;
+        pos[i] = r < n ? s_pos[r] : -1;
+      }
+      typename E::Frag kf[RPI], vf[RPI];
+#pragma unroll
+      for (int i = 0; i < RPI; i++) kf[i] = E::load(kb + (size_t)max(pos[i], 0) * tok);
+#pragma unroll
+      for (int i = 0; i < RPI; i++) vf[i] = E::load(vb + (size_t)max(pos[i], 0) * tok);
+      float u[RPI][G];
+#pragma unroll
+      for (int i = 0; i < RPI; i++)
+#pragma unroll
+        for (int h = 0; h < G; h++) {
+          const float sc = dpp_sum16(E::dot(qf[h], kf[i]));
+          u[i][h] = pos[i] >= 0 ? sc * c_log2 : -INFINITY;
+        }
+      float v[RPI][8];
+#pragma unroll
+      for (int i = 0; i < RPI; i++) E::to_f32(vf[i], v[i]);
+      st.update(u, v);
+    }
+  }
+  // Merge the 4 lane groups: lanes sub, sub+16, sub+32, sub+48.
+  st.merge_xor(16);
+  st.merge_xor(32);
+  if (rg != 0) return;
+#pragma unroll
+  for (int h = 0; h < G; h++) {
+    const size_t head = (size_t)bt * Hq + g * G + h;
+    if (S == 1) {
+      float x[8];
+      const float inv = st.l[h] > 0.f ? 1.f / st.l[h] : 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; e++) x[e] = st.o[h][e] * inv;
+      E::store8(out, head * kD + 8 * sub, x);
+      if (sub == 0 && lse)
+        lse[head] = st.l[h] > 0.f ? (st.m[h] + log2f(st.l[h])) * kLn2 : -INFINITY;
+    } else {
+      float* rec = partials + (head * S + split) * kPart;
+      float4* o4 = reinterpret_cast<float4*>(rec + 4 + 8 * sub);
+      o4[0] = make_float4(st.o[h][0], st.o[h][1], st.o[h][2], st.o[h][3]);
+      o4[1] = make_float4(st.o[h][4], st.o[h][5], st.o[h][6], st.o[h][7]);
+      if (sub == 0) {
+        rec[0] = st.m[h];
+        rec[1] = st.l[h];
+      }
+    }
+  }
+}
+
+// Merges the S split states of each (query, head), S <= kMaxSplits.
+// grid (B*T*Hq), block D. The split weights exp2(m_s - M) go to LDS first so
+// the S loads of each output element are independent of one another.
+template <int DT>
+__global__ __launch_bounds__(kD) void attn_combine_kernel(const float* __restrict__ partials,
+                                                          void* __restrict__ out,
+                                                          float* __restrict__ lse, int S) {
+  using E = AttnElem<DT>;
+  __shared__ float wgt[kMaxSplits];
+  __shared__ float red[2];
+  const size_t head = blockIdx.x;
+  const int d = threadIdx.x;
+  const int wave = d / kWave;
+  const float* rec = partials + head * S * kPart;
+  float mv[2], lv[2];
+#pragma unroll
+  for (int j = 0; j < 2; j++) {
+    const int s = d + j * kD;
+    mv[j] = s < S ? rec[(size_t)s * kPart] : -INFINITY;
+    lv[j] = s < S ? rec[(size_t)s * kPart + 1] : 0.f;
+  }
+  float M = fmaxf(mv[0], mv[1]);
+  for (int off = kWave / 2; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, kWave));
+  if (d % kWave == 0) red[wave] = M;
+  __syncthreads();
+  M = fmaxf(red[0], red[1]);
+  float Ls = 0.f;
+#pragma unroll
+  for (int j = 0; j < 2; j++) {
+    const int s = d + j * kD;
+    const float a = rescale(mv[j], M);
+    if (s < S) wgt[s] = a;
+    Ls += lv[j] * a;
+  }
+  for (int off = kWave / 2; off > 0; off >>= 1) Ls += __shfl_xor(Ls, off, kWave);
+  __syncthreads();  // red[] reads of M done; wgt[] written
+  if (d % kWave == 0) red[wave] = Ls;
+  __syncthreads();
+  const float L = red[0] + red[1];
+  float O = 0.f;
+#pragma unroll 16
+  for (int s = 0; s < S; s++) O += rec[(size_t)s * kPart + 4 + d] * wgt[s];
+  E::store(out, head * kD + d, L > 0.f ? O / L : 0.f);
+  if (d == 0 && lse) lse[head] = L > 0.f ? (M + log2f(L)) * kLn2 : -INFINITY;
+}
+
+// Block-table gather path (dense attention over every position of the
+// listed blocks): one workgroup per (query, KV head), 4 waves, no split.
+struct BlockSrc {
+  const int32_t* indptr;
+  const int32_t* indices;
+  int block, T, Hkv;
+};
+
+template <int DT, int G>
+__global__ __launch_bounds__(256) void block_gather_kernel(
+    const char* __restrict__ q, const char* __restrict__ kc, const char* __restrict__ vc,
+    BlockSrc src, void* __restrict__ out, float* __restrict__ lse, int T, int Hkv, int kv_len,
+    int L_cap, float c_log2) {
+  using E = AttnElem<DT>;
+  constexpr int ROW = kD * E::bytes;
+  const int lane = threadIdx.x % kWave;
+  const int wave = threadIdx.x / kWave;
+  const int sub = lane % 16, rg = lane / 16;
+  const int g = blockIdx.y, bt = blockIdx.z;
+  const int b = bt / T, t = bt % T;
+  const int vis = kv_len - T + t + 1;
+  const int Hq = Hkv * G;
+  const int u = b * Hkv + g;
+  const int32_t* list = src.indices + src.indptr[u];
+  const int n = (src.indptr[u + 1] - src.indptr[u]) * src.block;
+
+  typename E::Frag qf[G];
+#pragma unroll
+  for (int h = 0; h < G; h++)
+    qf[h] = E::load(q + (((size_t)bt * Hq + g * G + h) * kD + 8 * sub) * E::bytes);
+  HeadState<G> st;
+  st.init();
+  const char* kb = kc + ((size_t)b * L_cap * Hkv + g) * ROW + 8 * sub * E::bytes;
+  const char* vb = vc + ((size_t)b * L_cap * Hkv + g) * ROW + 8 * sub * E::bytes;
+  const size_t tok = (size_t)Hkv * ROW;
+  for (int wb = wave * 16; wb < n; wb += 64) {  // wave-uniform
+    int pos[4];
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      const int r = wb + rg * 4 + i;
+      const int p = r < n ? list[r / src.block] * src.block + r % src.block : -1;
+      pos[i] = (p >= 0 && p < vis) ? p : -1;
+    }
+    typename E::Frag kf[4], vf[4];
+#pragma unroll
+    for (int i = 0; i < 4; i++) kf[i] = E::load(kb + (size_t)max(pos[i], 0) * tok);
+#pragma unroll
+    for (int i = 0; i < 4; i++) vf[i] = E::load(vb + (size_t)max(pos[i], 0) * tok);
+    float uu[4][G];
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+#pragma unroll
+      for (int h = 0; h < G; h++) {
+        const float sc = dpp_sum16(E::dot(qf[h], kf[i]));
+        uu[i][h] = pos[i] >= 0 ? sc * c_log2 : -INFINITY;
+      }
+    float v[4][8];
+#pragma unroll
+    for (int i = 0; i < 4; i++) E::to_f32(vf[i], v[i]);
+    st.update(uu, v);
+  }
+  st.merge_xor(16);
+  st.merge_xor(32);
+  __shared__ float sh[4][G][kD + 2];
   if (lane < 16) {
 #pragma unroll
     for (int h = 0; h < G; h++) {
 #pragma unroll
-      for (int e = 0; e < 8; e++) st[wave][h][2 + 8 * sub + e] = o[h][e];
+      for (int e = 0; e < 8; e++) sh[wave][h][2 + 8 * sub + e] = st.o[h][e];
       if (sub == 0) {
-        st[wave][h][0] = m[h];
-        st[wave][h][1] = l[h];
+        sh[wave][h][0] = st.m[h];
+        sh[wave][h][1] = st.l[h];
       }
     }
   }
   __syncthreads();
-
-  const size_t unit = (size_t)bt * Hkv + g;  // (query, KV head)
-  float* part = partials + (unit * S + split) * (G * (kD + 2));
   for (int item = threadIdx.x; item < G * kD; item += blockDim.x) {
     const int h = item / kD, d = item % kD;
     float M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < 4; w++) M = fmaxf(M, st[w][h][0]);
+    for (int w = 0; w < 4; w++) M = fmaxf(M, sh[w][h][0]);
     float L = 0.f, O = 0.f;
 #pragma unroll
     for (int w = 0; w < 4; w++) {
-      const float a = rescale(st[w][h][0], M);
-      L += st[w][h][1] * a;
-      O += st[w][h][2 + d] * a;
+      const float a = rescale(sh[w][h][0], M);
+      L += sh[w][h][1] * a;
+      O += sh[w][h][2 + d] * a;
     }
-    if (S == 1) {
-      const size_t oi = ((size_t)bt * Hq + g * G + h) * kD + d;
-      E::store(out, oi, L > 0.f ? O / L : 0.f);
-      if (d == 0 && lse) lse[(size_t)bt * Hq + g * G + h] = L > 0.f ? (M + log2f(L)) * kLn2 : -INFINITY;
-    } else {
-      part[h * (kD + 2) + 2 + d] = O;
-      if (d == 0) {
-        part[h * (kD + 2)] = M;
-        part[h * (kD + 2) + 1] = L;
-      }
-    }
+    const size_t head = (size_t)bt * Hq + g * G + h;
+    E::store(out, head * kD + d, L > 0.f ? O / L : 0.f);
+    if (d == 0 && lse) lse[head] = L > 0.f ? (M + log2f(L)) * kLn2 : -INFINITY;
   }
-  if (S == 1) return;
-
-  // Split combine by the last workgroup to finish this (query, KV head).
-  __threadfence();
-  __syncthreads();
-  if (threadIdx.x == 0) s_last = atomicAdd(&counters[unit], 1u) == (uint32_t)(S - 1);
-  __syncthreads();
-  if (!s_last) return;
-  __threadfence();
-  const float* pu = partials + unit * S * (G * (kD + 2));
-  for (int item = threadIdx.x; item < G * kD; item += blockDim.x) {
-    const int h = item / kD, d = item % kD;
-    float M = -INFINITY;
-    for (int s = 0; s < S; s++) M = fmaxf(M, pu[(size_t)s * G * (kD + 2) + h * (kD + 2)]);
-    float L = 0.f, O = 0.f;
-    for (int s = 0; s < S; s++) {
-      const float* ps = pu + (size_t)s * G * (kD + 2) + h * (kD + 2);
-      const float a = rescale(ps[0], M);
-      L += ps[1] * a;
-      O += ps[2 + d] * a;
-    }
-    const size_t oi = ((size_t)bt * Hq + g * G + h) * kD + d;
-    E::store(out, oi, L > 0.f ? O / L : 0.f);
-    if (d == 0 && lse) lse[(size_t)bt * Hq + g * G + h] = L > 0.f ? (M + log2f(L)) * kLn2 : -INFINITY;
-  }
-  if (threadIdx.x == 0) counters[unit] = 0u;
 }
 
-template <int DT, int G, class Src>
-int launch_g(const void* q, const void* kc, const void* vc, Src src, void* out, float* lse,
-             int B, int T, int Hkv, int kv_len, int L_cap, float c_log2, int splits,
-             int rows_per_split, uint32_t* counters, float* partials, hipStream_t stream) {
-  dim3 grid(splits, Hkv, B * T);
-  hipLaunchKernelGGL((sparse_attn_kernel<DT, G, Src>), grid, dim3(kAttnThreads), 0, stream,
+// Waves per workgroup: the largest divisor of Hkv that is at most kMaxWaves.
+int waves_for(int Hkv) {
+  for (int w = kMaxWaves; w > 1; w--)
+    if (Hkv % w == 0) return w;
+  return 1;
+}
+
+template <int DT, int G>
+int launch_index_path(const void* q, const void* kc, const void* vc, const int32_t* idx, int k,
+                      void* out, float* lse, int B, int T, int Hkv, int kv_len, int L_cap,
+                      float c_log2, const AttnSplit& sp, float* partials, hipStream_t stream) {
+  const int nw = waves_for(Hkv);
+  dim3 grid(sp.splits, B * T, Hkv / nw);
+  hipLaunchKernelGGL((attn_split_kernel<DT, G>), grid, dim3(kWave * nw), 0, stream,
                      static_cast<const char*>(q), static_cast<const char*>(kc),
-                     static_cast<const char*>(vc), src, out, lse, T, Hkv, kv_len, L_cap, c_log2,
-                     rows_per_split, counters, partials);
-  return check_launch("sparse_attn");
+                     static_cast<const char*>(vc), idx, k, out, lse, T, Hkv, kv_len, L_cap, c_log2,
+                     sp.rows_per_split, partials);
+  int rc = check_launch("attn_split");
+  if (rc || sp.splits == 1) return rc;
+  hipLaunchKernelGGL((attn_combine_kernel<DT>), dim3(B * T * Hkv * G), dim3(kD), 0, stream,
+                     partials, out, lse, sp.splits);
+  return check_launch("attn_combine");
 }
 
-template <int DT, class Src>
-int launch_dt(int G, const void* q, const void* kc, const void* vc, Src src, void* out,
-              float* lse, int B, int T, int Hkv, int kv_len, int L_cap, float c_log2, int splits,
-              int rows, uint32_t* cnt, float* part, hipStream_t stream) {
+template <int DT>
+int dispatch_index_path(int G, const void* q, const void* kc, const void* vc, const int32_t* idx,
+                        int k, void* out, float* lse, int B, int T, int Hkv, int kv_len, int L_cap,
+                        float c_log2, const AttnSplit& sp, float* part, hipStream_t s) {
   switch (G) {
-    case 1: return launch_g<DT, 1>(q, kc, vc, src, out, lse, B, T, Hkv, kv_len, L_cap, c_log2, splits, rows, cnt, part, stream);
-    case 2: return launch_g<DT, 2>(q, kc, vc, src, out, lse, B, T, Hkv, kv_len, L_cap, c_log2, splits, rows, cnt, part, stream);
-    case 4: return launch_g<DT, 4>(q, kc, vc, src, out, lse, B, T, Hkv, kv_len, L_cap, c_log2, splits, rows, cnt, part, stream);
-    case 8: return launch_g<DT, 8>(q, kc, vc, src, out, lse, B, T, Hkv, kv_len, L_cap, c_log2, splits, rows, cnt, part, stream);
+    case 1: return launch_index_path<DT, 1>(q, kc, vc, idx, k, out, lse, B, T, Hkv, kv_len, L_cap, c_log2, sp, part, s);
+    case 2: return launch_index_path<DT, 2>(q, kc, vc, idx, k, out, lse, B, T, Hkv, kv_len, L_cap, c_log2, sp, part, s);
+    case 4: return launch_index_path<DT, 4>(q, kc, vc, idx, k, out, lse, B, T, Hkv, kv_len, L_cap, c_log2, sp, part, s);
+    case 8: return launch_index_path<DT, 8>(q, kc, vc, idx, k, out, lse, B, T, Hkv, kv_len, L_cap, c_log2, sp, part, s);
   }
-  return set_error(CLSA_ERR_UNSUPPORTED, "attention: Hq/Hkv=%d", G);
+  return set_error(CLSA_ERR_UNSUPPORTED, "sparse_attn: Hq/Hkv=%d", G);
+}
+
+template <int DT>
+int dispatch_block_path(int G, const void* q, const void* kc, const void* vc, BlockSrc src,
+                        void* out, float* lse, int B, int T, int Hkv, int kv_len, int L_cap,
+                        float c_log2, hipStream_t s) {
+  dim3 grid(1, Hkv, B * T);
+  const char *qq = static_cast<const char*>(q), *kk = static_cast<const char*>(kc),
+             *vv = static_cast<const char*>(vc);
+  switch (G) {
+    case 1: hipLaunchKernelGGL((block_gather_kernel<DT, 1>), grid, dim3(256), 0, s, qq, kk, vv, src, out, lse, T, Hkv, kv_len, L_cap, c_log2); break;
+    case 2: hipLaunchKernelGGL((block_gather_kernel<DT, 2>), grid, dim3(256), 0, s, qq, kk, vv, src, out, lse, T, Hkv, kv_len, L_cap, c_log2); break;
+    case 4: hipLaunchKernelGGL((block_gather_kernel<DT, 4>), grid, dim3(256), 0, s, qq, kk, vv, src, out, lse, T, Hkv, kv_len, L_cap, c_log2); break;
+    case 8: hipLaunchKernelGGL((block_gather_kernel<DT, 8>), grid, dim3(256), 0, s, qq, kk, vv, src, out, lse, T, Hkv, kv_len, L_cap, c_log2); break;
+    default: return set_error(CLSA_ERR_UNSUPPORTED, "block attention: Hq/Hkv=%d", G);
+  }
+  return check_launch("block_gather");
 }
 
 }  // namespace
@@ -343,50 +504,56 @@ bool sparse_attn_supported(int dtype, int Hq, int Hkv, int D) {
   return G == 1 || G == 2 || G == 4 || G == 8;
 }
 
+// Splits of the k entries: about one workgroup per CU (256), each wave
+// taking a multiple of 32 entries (one 8-row step of its 4 lane groups), at
+// most kMaxSplits splits. Measured on MI355X: one 8-wave workgroup per CU
+// beat both fewer, longer splits and two workgroups per CU at B = 4, 8, 16.
 AttnSplit attn_split(int B, int T, int Hkv, int k) {
   AttnSplit L;
-  const long units = (long)B * T * Hkv;
-  const int max_splits = (k + kRowsPerStep - 1) / kRowsPerStep;
-  long s = (1024 + units - 1) / units;
+  const long units = (long)B * T * (Hkv / waves_for(Hkv));
+  const int step = 32;
+  int max_splits = (k + step - 1) / step;
+  if (max_splits > kMaxSplits) max_splits = kMaxSplits;
+  long s = (256 + units - 1) / units;
   if (s > max_splits) s = max_splits;
   if (s < 1) s = 1;
   int rows = (int)((k + s - 1) / s);
-  rows = (rows + kRowsPerStep - 1) / kRowsPerStep * kRowsPerStep;
+  rows = (rows + step - 1) / step * step;
   L.rows_per_split = rows;
   L.splits = (k + rows - 1) / rows;
   return L;
 }
 
-int launch_sparse_attn(const void* q, const void* kc, const void* vc, int dtype, const int32_t* idx,
-                       int k, void* out, float* lse, int B, int T, int Hq, int Hkv, int D,
-                       int kv_len, int L_cap, float scale, uint32_t* counters, float* partials,
-                       hipStream_t stream) {
-  const AttnSplit Lo = attn_split(B, T, Hkv, k);
-  const float c_log2 = (scale > 0.f ? scale : 1.f / sqrtf((float)D)) * kLog2e;
-  const int G = Hq / Hkv;
-  IdxSrc src{idx, k, nullptr};
-  if (dtype == CLSA_BF16)
-    return launch_dt<CLSA_BF16>(G, q, kc, vc, src, out, lse, B, T, Hkv, kv_len, L_cap, c_log2,
-                                Lo.splits, Lo.rows_per_split, counters, partials, stream);
-  return launch_dt<CLSA_F32>(G, q, kc, vc, src, out, lse, B, T, Hkv, kv_len, L_cap, c_log2,
-                             Lo.splits, Lo.rows_per_split, counters, partials, stream);
+size_t attn_partial_floats(int B, int T, int Hq, int Hkv, int k) {
+  const AttnSplit s = attn_split(B, T, Hkv, k);
+  return s.splits > 1 ? (size_t)B * T * Hq * s.splits * kPart : 0;
 }
 
-// Dense attention over block-table positions, one workgroup per (query, KV
-// head), no split. Positions past the query's visible range are skipped.
+int launch_sparse_attn(const void* q, const void* kc, const void* vc, int dtype, const int32_t* idx,
+                       int k, void* out, float* lse, int B, int T, int Hq, int Hkv, int D,
+                       int kv_len, int L_cap, float scale, float* partials, hipStream_t stream) {
+  const AttnSplit sp = attn_split(B, T, Hkv, k);
+  const float c_log2 = (scale > 0.f ? scale : 1.f / sqrtf((float)D)) * kLog2e;
+  const int G = Hq / Hkv;
+  if (dtype == CLSA_BF16)
+    return dispatch_index_path<CLSA_BF16>(G, q, kc, vc, idx, k, out, lse, B, T, Hkv, kv_len, L_cap,
+                                          c_log2, sp, partials, stream);
+  return dispatch_index_path<CLSA_F32>(G, q, kc, vc, idx, k, out, lse, B, T, Hkv, kv_len, L_cap,
+                                       c_log2, sp, partials, stream);
+}
+
 int launch_block_attn_gather(const void* q, const void* kc, const void* vc, int dtype,
                              const int32_t* kv_indptr, const int32_t* kv_indices, int block,
                              void* out, float* lse, int B, int T, int Hq, int Hkv, int D,
                              int kv_len, int L_cap, float scale, hipStream_t stream) {
   const float c_log2 = (scale > 0.f ? scale : 1.f / sqrtf((float)D)) * kLog2e;
   const int G = Hq / Hkv;
-  BlockSrc src{kv_indptr, kv_indices, block, T, Hkv, nullptr, 0};
-  const int rows = 1 << 30;  // one split covers the whole table
+  BlockSrc src{kv_indptr, kv_indices, block, T, Hkv};
   if (dtype == CLSA_BF16)
-    return launch_dt<CLSA_BF16>(G, q, kc, vc, src, out, lse, B, T, Hkv, kv_len, L_cap, c_log2, 1,
-                                rows, nullptr, nullptr, stream);
-  return launch_dt<CLSA_F32>(G, q, kc, vc, src, out, lse, B, T, Hkv, kv_len, L_cap, c_log2, 1,
-                             rows, nullptr, nullptr, stream);
+    return dispatch_block_path<CLSA_BF16>(G, q, kc, vc, src, out, lse, B, T, Hkv, kv_len, L_cap,
+                                          c_log2, stream);
+  return dispatch_block_path<CLSA_F32>(G, q, kc, vc, src, out, lse, B, T, Hkv, kv_len, L_cap,
+                                       c_log2, stream);
 }
 
 }  // namespace clsa

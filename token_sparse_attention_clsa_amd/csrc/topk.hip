@@ -5,38 +5,40 @@
 // "1. Problématique"), ties to the lower position, output ascending, -1
 // padding when fewer than k positions are visible.
 //
-// Scores become order-preserving 32-bit keys (-0 folded onto +0) and the
-// k-th largest key theta is found by radix selection on three digits:
-// bits 31..20, 19..8 and 7..0. Three launches:
-//   1. topk_hist  (chunks x rows): per-row histogram of the top digit. Each
-//      workgroup counts one 4096-element chunk in LDS and adds its non-zero
-//      bins to the row histogram with global atomics (integer counts, so the
-//      result does not depend on arrival order).
-//   2. topk_part  (chunks x rows): every workgroup finds the threshold bin
-//      b0 from the row histogram and writes, in position order, the
-//      positions of its chunk whose top digit is >= b0 (a superset of the
-//      answer, typically k plus one bin's worth) into the chunk's segment of
-//      a candidate list, plus the segment's length.
-//   3. topk_final (rows): one 1024-thread workgroup per row gathers the
-//      candidate segments (in chunk order, hence position order) into LDS,
-//      resolves the two low digits by LDS histograms, and emits the k
-//      positions with one ordered scan: keys above theta always, keys equal
-//      to theta for the first `quota` of them in position order. It then
-//      clears the row histogram, leaving the workspace ready for the next
-//      call.
-// Rows whose visible count is <= k skip the selection: every visible
-// position is a candidate and is emitted in order.
+// Scores become order-preserving 32-bit keys (-0 folded onto +0); selection
+// is radix selection on three digits (bits 31..20, 19..8, 7..0). Two
+// launches:
+//   1. topk_filter (chunks x rows, 256 threads): every workgroup of a row
+//      takes the same deterministic strided sample of the row, histograms the
+//      sample's top digits in LDS and picks the bin where the sample's count
+//      from the top reaches about twice the rank k would have in the sample.
+//      It then writes, in position order, the positions of its 4096-element
+//      chunk whose top digit is at or above that bin, and their count. With a
+//      2048-element sample the chance that this keeps fewer than k positions
+//      is negligible for any smooth score distribution, and the next kernel
+//      checks it anyway.
+//   2. topk_select (rows, 1024 threads): gathers the candidate segments (in
+//      chunk order, hence position order) into LDS and resolves the k-th key
+//      theta exactly with three LDS histograms, then emits, in one ordered
+//      scan, keys above theta and the first `quota` keys equal to theta. If
+//      the candidates number fewer than k, it redoes the row on its own (LDS
+//      histogram of the full row, ordered candidate pass), so the result is
+//      exact whatever the sample did.
+// Rows whose visible count is <= k take every visible position.
 #include "kernels.h"
 
 namespace clsa {
 namespace {
 
-constexpr int kBins0 = kTopkBins;       // top digit: 12 bits
-constexpr int kChunk = kTopkChunk;      // elements per chunk
-constexpr int kPartThreads = 256;       // 16 consecutive elements per thread
-constexpr int kFinalThreads = 1024;
-constexpr int kMaxChunks = kTopkMaxChunks;  // kv_len <= 4M
-constexpr int kLdsCap = 12288;          // candidates gathered into LDS
+constexpr int kBins0 = kTopkBins;  // top digit: 12 bits
+constexpr int kThreads = 1024;     // topk_select
+constexpr int kWaves = kThreads / kWave;
+constexpr int kFilterThreads = 256;
+constexpr int kChunk = kTopkChunk; // topk_filter: 16 consecutive elements per thread
+constexpr int kSample = 2048;      // strided sample for the threshold estimate
+constexpr int kTile = 16384;       // fallback tile: 16 waves x 1024 consecutive elements
+constexpr int kLdsCap = 12288;     // candidates kept in LDS
+constexpr int kHistCopies = 2;     // fallback histogram copies
 
 // Finds the bin b (scanning bins from high to low) where the running count
 // first reaches `need`; res[0] = b, res[1] = count in bins above b.
@@ -51,7 +53,7 @@ __device__ void find_bin(const uint32_t* h, int nbins, int need, int* res, int* 
   const int before = block_exclusive_scan(sum, tmp, &total);
   if (before < need && need <= before + sum) {
     int acc = before;
-    for (int j = 0; j < per; j++) {
+    for (int j = 0; j < per && hi - j >= 0; j++) {
       const int c = h[hi - j];
       if (acc + c >= need) {
         res[0] = hi - j;
@@ -70,90 +72,31 @@ __global__ __launch_bounds__(256) void fill_zero(uint32_t* p, size_t n) {
     p[i] = 0u;
 }
 
-// grid (nchunks, rows), block 256.
-__global__ __launch_bounds__(kPartThreads) void topk_hist(const float* __restrict__ scores,
-                                                          uint32_t* __restrict__ ghist, int T,
-                                                          int kv_len) {
-  __shared__ uint32_t h[kBins0];
-  const int row = blockIdx.y;
-  const int vis = kv_len - T + (row % T) + 1;
-  const int c0 = blockIdx.x * kChunk;
-  if (c0 >= vis) return;
-  for (int i = threadIdx.x; i < kBins0; i += blockDim.x) h[i] = 0u;
-  __syncthreads();
-  const float* sr = scores + (size_t)row * kv_len;
-  const int c1 = min(c0 + kChunk, vis);
-  for (int s = c0 + threadIdx.x; s < c1; s += blockDim.x) atomicAdd(&h[score_key(sr[s]) >> 20], 1u);
-  __syncthreads();
-  uint32_t* gh = ghist + (size_t)row * kBins0;
-  for (int i = threadIdx.x; i < kBins0; i += blockDim.x)
-    if (h[i]) atomicAdd(&gh[i], h[i]);
-}
-
-// grid (nchunks, rows), block 256.
-__global__ __launch_bounds__(kPartThreads) void topk_part(const float* __restrict__ scores,
-                                                          const uint32_t* __restrict__ ghist,
-                                                          uint32_t* __restrict__ counts,
-                                                          int32_t* __restrict__ cand, int T,
-                                                          int kv_len, int k, int nchunks) {
-  __shared__ uint32_t h[kBins0];
-  __shared__ int tmp[17];
-  __shared__ int res[2];
-  const int row = blockIdx.y;
-  const int vis = kv_len - T + (row % T) + 1;
-  const int c0 = blockIdx.x * kChunk;
-  if (c0 >= vis) {
-    if (threadIdx.x == 0) counts[(size_t)row * nchunks + blockIdx.x] = 0u;
-    return;
-  }
-  uint32_t b0 = 0;  // every visible element qualifies when vis <= k
-  if (vis > k) {
-    const uint32_t* gh = ghist + (size_t)row * kBins0;
-    for (int i = threadIdx.x; i < kBins0; i += blockDim.x) h[i] = gh[i];
-    __syncthreads();
-    find_bin(h, kBins0, k, res, tmp);
-    b0 = (uint32_t)res[0];
-  }
-  const float* sr = scores + (size_t)row * kv_len;
-  const int e0 = c0 + threadIdx.x * 16;
-  uint32_t flags = 0;
-  int cnt = 0;
-#pragma unroll
-  for (int j = 0; j < 16; j++) {
-    const int s = e0 + j;
-    if (s < vis && (score_key(sr[s]) >> 20) >= b0) {
-      flags |= 1u << j;
-      cnt++;
-    }
-  }
-  int total;
-  int off = block_exclusive_scan(cnt, tmp, &total);
-  int32_t* seg = cand + ((size_t)row * nchunks + blockIdx.x) * kChunk;
-#pragma unroll
-  for (int j = 0; j < 16; j++)
-    if (flags >> j & 1u) seg[off++] = e0 + j;
-  if (threadIdx.x == 0) counts[(size_t)row * nchunks + blockIdx.x] = (uint32_t)total;
-}
-
-// Candidate accessors for topk_final: LDS copy, or the segmented global list.
-struct LdsCand {
-  const int32_t* pos;
-  const uint32_t* key;
-  __device__ int p(int i) const { return pos[i]; }
-  __device__ uint32_t k(int i) const { return key[i]; }
+// Candidates: the first kLdsCap in LDS, the rest in the workspace (their
+// keys are read back from the scores).
+struct Cand {
+  const int32_t* lpos;
+  const uint32_t* lkey;
+  const int32_t* gpos;
+  const float* srow;
+  __device__ int p(int i) const { return i < kLdsCap ? lpos[i] : gpos[i]; }
+  __device__ uint32_t k(int i) const { return i < kLdsCap ? lkey[i] : score_key(srow[gpos[i]]); }
 };
-struct GlobalCand {
-  const int32_t* seg;     // row's segments, kChunk entries each
-  const int* chunk_off;   // LDS, nchunks + 1 exclusive offsets
+
+// Candidates still in the filter's chunk segments: candidate i lives in the
+// chunk c with off[c] <= i < off[c + 1].
+struct SegCand {
+  const int32_t* seg;  // the row's segments, kChunk entries each
+  const int* off;      // LDS, nchunks + 1 exclusive offsets
   int nchunks;
   const float* srow;
   __device__ int p(int i) const {
-    int lo = 0, hi = nchunks;  // largest c with chunk_off[c] <= i
+    int lo = 0, hi = nchunks;
     while (hi - lo > 1) {
       const int mid = (lo + hi) / 2;
-      if (chunk_off[mid] <= i) lo = mid; else hi = mid;
+      if (off[mid] <= i) lo = mid; else hi = mid;
     }
-    return seg[(size_t)lo * kChunk + (i - chunk_off[lo])];
+    return seg[(size_t)lo * kChunk + (i - off[lo])];
   }
   __device__ uint32_t k(int i) const { return score_key(srow[p(i)]); }
 };
@@ -161,7 +104,7 @@ struct GlobalCand {
 // Resolves theta among the candidates and emits the row's selection.
 template <class Acc>
 __device__ void select_and_emit(const Acc& acc, int n, int need0, uint32_t b0, uint32_t* h,
-                                int* res, int* tmp, int32_t* out) {
+                                int* res, int* tmp, int32_t* out, int k) {
   // Digit 1 (bits 19..8) among candidates whose top digit is b0.
   for (int i = threadIdx.x; i < kBins0; i += blockDim.x) h[i] = 0u;
   __syncthreads();
@@ -205,10 +148,11 @@ __device__ void select_and_emit(const Acc& acc, int n, int need0, uint32_t b0, u
       if (i0 + e < n) {
         const uint32_t key = acc.k(i0 + e);
         if (key > theta) {
-          out[g + min(q, quota)] = acc.p(i0 + e);
+          const int o = g + min(q, quota);
+          if (o < k) out[o] = acc.p(i0 + e);
           g++;
         } else if (key == theta) {
-          if (q < quota) out[g + q] = acc.p(i0 + e);
+          if (q < quota && g + q < k) out[g + q] = acc.p(i0 + e);
           q++;
         }
       }
@@ -218,61 +162,246 @@ __device__ void select_and_emit(const Acc& acc, int n, int need0, uint32_t b0, u
   }
 }
 
-// grid (rows), block 1024.
-__global__ __launch_bounds__(kFinalThreads) void topk_final(const float* __restrict__ scores,
-                                                            uint32_t* __restrict__ ghist,
-                                                            const uint32_t* __restrict__ counts,
-                                                            const int32_t* __restrict__ cand,
-                                                            int32_t* __restrict__ idx, int T,
-                                                            int kv_len, int k, int nchunks) {
+// Full three-level selection of the k largest among n candidates.
+template <class Acc>
+__device__ void select_top(const Acc& acc, int n, int k, uint32_t* h, int* res, int* tmp,
+                           int32_t* out) {
+  for (int i = threadIdx.x; i < kBins0; i += blockDim.x) h[i] = 0u;
+  __syncthreads();
+  for (int i = threadIdx.x; i < n; i += blockDim.x) atomicAdd(&h[acc.k(i) >> 20], 1u);
+  __syncthreads();
+  find_bin(h, kBins0, k, res, tmp);
+  const uint32_t b0 = (uint32_t)res[0];
+  const int need0 = k - res[1];
+  __syncthreads();  // everyone has read res before select_and_emit reuses it
+  select_and_emit(acc, n, need0, b0, h, res, tmp, out, k);
+}
+
+template <bool VEC>
+__device__ __forceinline__ void load4(const float* srow, int e, int vis, float* x) {
+  if (VEC && e + 3 < vis) {
+    const float4 v = *reinterpret_cast<const float4*>(srow + e);
+    x[0] = v.x; x[1] = v.y; x[2] = v.z; x[3] = v.w;
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; j++) x[j] = e + j < vis ? srow[e + j] : 0.f;
+  }
+}
+
+// Pass 1 and pass 2 over one row (see the file comment).
+template <bool VEC>
+__device__ int histogram_and_candidates(const float* srow, int vis, int k, uint32_t* h,
+                                        int32_t* lpos, uint32_t* lkey, int32_t* gpos,
+                                        int* wtot, int* tmp, int* res, uint32_t* b0_out,
+                                        int* above_out) {
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  // kHistCopies histograms side by side (scores cluster in a few bins; spreading
+  // the waves over copies cuts same-address atomic serialisation), summed into h.
+  uint32_t* hc = h + kBins0 * (1 + wave % kHistCopies);
+  for (int i = threadIdx.x; i < kBins0 * (1 + kHistCopies); i += kThreads) h[i] = 0u;
+  __syncthreads();
+  constexpr int kBatch = 8;  // float4 loads in flight per thread
+  for (int e0 = 4 * threadIdx.x; e0 < vis; e0 += 4 * kThreads * kBatch) {
+    float x[kBatch][4];
+#pragma unroll
+    for (int u = 0; u < kBatch; u++) load4<VEC>(srow, e0 + u * 4 * kThreads, vis, x[u]);
+#pragma unroll
+    for (int u = 0; u < kBatch; u++)
+#pragma unroll
+      for (int j = 0; j < 4; j++)
+        if (e0 + u * 4 * kThreads + j < vis) atomicAdd(&hc[score_key(x[u][j]) >> 20], 1u);
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < kBins0; i += kThreads) {
+    uint32_t c = 0;
+#pragma unroll
+    for (int r = 1; r <= kHistCopies; r++) c += h[kBins0 * r + i];
+    h[i] = c;
+  }
+  __syncthreads();
+  find_bin(h, kBins0, k, res, tmp);
+  const uint32_t b0 = (uint32_t)res[0];
+  *b0_out = b0;
+  *above_out = res[1];
+
+  int total = 0;
+  for (int t0 = 0; t0 < vis; t0 += kTile) {  // uniform over the workgroup
+    // wave w owns [seg, seg + 1024) in 4 steps of 256; lane l owns 4 consecutive elements per step
+    const int seg = t0 + wave * 1024;
+    uint32_t flags[4];
+    uint32_t keys[4][4];
+    int step_off[4], step_tot[4];
+    int wave_total = 0;
+    float xs[4][4];
+#pragma unroll
+    for (int st = 0; st < 4; st++) load4<VEC>(srow, seg + st * 256 + 4 * lane, vis, xs[st]);
+#pragma unroll
+    for (int st = 0; st < 4; st++) {
+      const int e = seg + st * 256 + 4 * lane;
+      const float* x = xs[st];
+      flags[st] = 0;
+      int c = 0;
+#pragma unroll
+      for (int j = 0; j < 4; j++) {
+        keys[st][j] = score_key(x[j]);
+        if (e + j < vis && (keys[st][j] >> 20) >= b0) {
+          flags[st] |= 1u << j;
+          c++;
+        }
+      }
+      const int inc = wave_inclusive_scan(c);
+      step_off[st] = wave_total + inc - c;
+      step_tot[st] = __shfl(inc, kWave - 1, kWave);
+      wave_total += step_tot[st];
+    }
+    if (lane == 0) wtot[wave] = wave_total;
+    __syncthreads();
+    if (wave == 0) {
+      const int v = lane < kWaves ? wtot[lane] : 0;
+      const int inc = wave_inclusive_scan(v);
+      if (lane < kWaves) wtot[lane] = inc - v;  // exclusive base of each wave
+      if (lane == kWaves - 1) wtot[kWaves] = inc;
+    }
+    __syncthreads();
+    const int base = total + wtot[wave];
+#pragma unroll
+    for (int st = 0; st < 4; st++) {
+      int o = base + step_off[st];
+      const int e = seg + st * 256 + 4 * lane;
+#pragma unroll
+      for (int j = 0; j < 4; j++) {
+        if (flags[st] >> j & 1u) {
+          if (o < kLdsCap) {
+            lpos[o] = e + j;
+            lkey[o] = keys[st][j];
+          } else {
+            gpos[o] = e + j;
+          }
+          o++;
+        }
+      }
+    }
+    total += wtot[kWaves];
+    __syncthreads();  // wtot is rewritten by the next tile
+  }
+  return total;
+}
+
+// grid (nchunks, rows), block 256.
+__global__ __launch_bounds__(kFilterThreads) void topk_filter(const float* __restrict__ scores,
+                                                              uint32_t* __restrict__ counts,
+                                                              int32_t* __restrict__ cand, int T,
+                                                              int kv_len, int k, int nchunks) {
   __shared__ uint32_t h[kBins0];
-  __shared__ int chunk_off[kMaxChunks + 1];
+  __shared__ int tmp[17];
+  __shared__ int res[2];
+  const int row = blockIdx.y;
+  const int vis = kv_len - T + (row % T) + 1;
+  const int c0 = blockIdx.x * kChunk;
+  uint32_t* cnt = counts + (size_t)row * nchunks + blockIdx.x;
+  if (vis <= k || c0 >= vis) {
+    if (threadIdx.x == 0) *cnt = 0u;
+    return;
+  }
+  const float* srow = scores + (size_t)row * kv_len;
+  // Threshold bin from the row's strided sample (identical in every workgroup).
+  for (int i = threadIdx.x; i < kBins0; i += blockDim.x) h[i] = 0u;
+  __syncthreads();
+  const int m = min(kSample, vis);
+  for (int i = threadIdx.x; i < m; i += blockDim.x)
+    atomicAdd(&h[score_key(srow[(int)((long)i * vis / m)]) >> 20], 1u);
+  __syncthreads();
+  const long expect = ((long)k * m + vis - 1) / vis;  // rank of the k-th key in the sample
+  const int r = (int)min((long)m, 2 * expect + 8);
+  find_bin(h, kBins0, r, res, tmp);
+  const uint32_t b0 = (uint32_t)res[0];
+  // Ordered compaction of this chunk's positions whose top digit is >= b0.
+  const int e0 = c0 + threadIdx.x * 16;
+  uint32_t flags = 0;
+  int c = 0;
+  if (e0 + 15 < vis && (reinterpret_cast<uintptr_t>(srow + e0) & 15) == 0) {
+    const float4* p4 = reinterpret_cast<const float4*>(srow + e0);
+    float4 v[4] = {p4[0], p4[1], p4[2], p4[3]};
+    const float* x = reinterpret_cast<const float*>(v);
+#pragma unroll
+    for (int j = 0; j < 16; j++)
+      if ((score_key(x[j]) >> 20) >= b0) {
+        flags |= 1u << j;
+        c++;
+      }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 16; j++)
+      if (e0 + j < vis && (score_key(srow[e0 + j]) >> 20) >= b0) {
+        flags |= 1u << j;
+        c++;
+      }
+  }
+  int total;
+  int o = block_exclusive_scan(c, tmp, &total);
+  int32_t* seg = cand + ((size_t)row * nchunks + blockIdx.x) * kChunk;
+#pragma unroll
+  for (int j = 0; j < 16; j++)
+    if (flags >> j & 1u) seg[o++] = e0 + j;
+  if (threadIdx.x == 0) *cnt = (uint32_t)total;
+}
+
+// grid (rows), block 1024.
+__global__ __launch_bounds__(kThreads) void topk_select(const float* __restrict__ scores,
+                                                        const uint32_t* __restrict__ counts,
+                                                        const int32_t* __restrict__ cand,
+                                                        int32_t* __restrict__ spill,
+                                                        int32_t* __restrict__ idx, int T,
+                                                        int kv_len, int k, int nchunks) {
+  __shared__ uint32_t h[kBins0 * (1 + kHistCopies)];
   __shared__ int32_t lpos[kLdsCap];
   __shared__ uint32_t lkey[kLdsCap];
+  __shared__ int off[kTopkMaxChunks + 1];
+  __shared__ int wtot[kWaves + 1];
   __shared__ int tmp[17];
   __shared__ int res[2];
   const int row = blockIdx.x;
   const int vis = kv_len - T + (row % T) + 1;
-  const float* srow = scores + (size_t)row * kv_len;
-  uint32_t* gh = ghist + (size_t)row * kBins0;
   int32_t* out = idx + (size_t)row * k;
-
-  // Offsets of the candidate segments (chunk order = position order).
-  int total;
+  if (vis <= k) {  // every visible position, in order
+    for (int i = threadIdx.x; i < k; i += kThreads) out[i] = i < vis ? i : -1;
+    return;
+  }
+  const float* srow = scores + (size_t)row * kv_len;
+  // Offsets of the candidate segments (nchunks <= kThreads).
+  int n;
   {
     const int c = threadIdx.x;
     const int v = c < nchunks ? (int)counts[(size_t)row * nchunks + c] : 0;
-    const int off = block_exclusive_scan(v, tmp, &total);
-    if (c < nchunks) chunk_off[c] = off;
-    if (c == 0) chunk_off[nchunks] = total;
+    const int o = block_exclusive_scan(v, tmp, &n);
+    if (c < nchunks) off[c] = o;
+    if (c == 0) off[nchunks] = n;
   }
   __syncthreads();
-  const int n = total;
-  GlobalCand gacc{cand + (size_t)row * nchunks * kChunk, chunk_off, nchunks, srow};
-
-  if (vis <= k) {
-    // Every visible position is selected, in order.
-    for (int i = threadIdx.x; i < k; i += blockDim.x) out[i] = i < n ? gacc.p(i) : -1;
-  } else {
-    for (int i = threadIdx.x; i < kBins0; i += blockDim.x) h[i] = gh[i];
-    __syncthreads();
-    find_bin(h, kBins0, k, res, tmp);
-    const uint32_t b0 = (uint32_t)res[0];
-    const int need0 = k - res[1];
+  if (n >= k) {
+    SegCand seg{cand + (size_t)row * nchunks * kChunk, off, nchunks, srow};
     if (n <= kLdsCap) {
-      for (int i = threadIdx.x; i < n; i += blockDim.x) {
-        const int p = gacc.p(i);
+      for (int i = threadIdx.x; i < n; i += kThreads) {
+        const int p = seg.p(i);
         lpos[i] = p;
         lkey[i] = score_key(srow[p]);
       }
       __syncthreads();
-      select_and_emit(LdsCand{lpos, lkey}, n, need0, b0, h, res, tmp, out);
+      select_top(Cand{lpos, lkey, nullptr, srow}, n, k, h, res, tmp, out);
     } else {
-      select_and_emit(gacc, n, need0, b0, h, res, tmp, out);
+      select_top(seg, n, k, h, res, tmp, out);
     }
+    return;
   }
-  // Leave the row histogram cleared for the next call.
-  for (int i = threadIdx.x; i < kBins0; i += blockDim.x) gh[i] = 0u;
+  // The sample overshot: redo this row from its scores alone.
+  int32_t* gpos = spill + (size_t)row * kv_len;
+  uint32_t b0;
+  int above;
+  if ((reinterpret_cast<uintptr_t>(srow) & 15) == 0)
+    n = histogram_and_candidates<true>(srow, vis, k, h, lpos, lkey, gpos, wtot, tmp, res, &b0, &above);
+  else
+    n = histogram_and_candidates<false>(srow, vis, k, h, lpos, lkey, gpos, wtot, tmp, res, &b0, &above);
+  select_and_emit(Cand{lpos, lkey, gpos, srow}, n, k - above, b0, h, res, tmp, out, k);
 }
 
 }  // namespace
@@ -285,22 +414,28 @@ int zero_words(uint32_t* p, size_t n, hipStream_t stream) {
   return check_launch("fill_zero");
 }
 
+TopkBuffers topk_buffers(int rows, int kv_len) {
+  TopkBuffers b;
+  b.nchunks = (kv_len + kChunk - 1) / kChunk;
+  b.counts_words = (size_t)rows * b.nchunks;
+  b.cand_words = (size_t)rows * b.nchunks * kChunk;
+  b.spill_words = (size_t)rows * kv_len;
+  return b;
+}
+
 int launch_topk(const float* scores, int B, int T, int kv_len, int k, int32_t* idx,
-                uint32_t* hist, uint32_t* counts, int32_t* cand, hipStream_t stream) {
+                uint32_t* counts, int32_t* cand, int32_t* spill, hipStream_t stream) {
   const int rows = B * T;
-  const int nchunks = topk_nchunks(kv_len);
-  if (nchunks > kMaxChunks)
-    return set_error(CLSA_ERR_UNSUPPORTED, "topk: kv_len=%d above %d", kv_len, kMaxChunks * kChunk);
-  int rc;
-  hipLaunchKernelGGL(topk_hist, dim3(nchunks, rows), dim3(kPartThreads), 0, stream, scores, hist,
-                     T, kv_len);
-  if ((rc = check_launch("topk_hist"))) return rc;
-  hipLaunchKernelGGL(topk_part, dim3(nchunks, rows), dim3(kPartThreads), 0, stream, scores, hist,
-                     counts, cand, T, kv_len, k, nchunks);
-  if ((rc = check_launch("topk_part"))) return rc;
-  hipLaunchKernelGGL(topk_final, dim3(rows), dim3(kFinalThreads), 0, stream, scores, hist, counts,
-                     cand, idx, T, kv_len, k, nchunks);
-  return check_launch("topk_final");
+  const TopkBuffers tb = topk_buffers(rows, kv_len);
+  if (tb.nchunks > kTopkMaxChunks)
+    return set_error(CLSA_ERR_UNSUPPORTED, "topk: kv_len=%d above %d", kv_len, kTopkMaxChunks * kChunk);
+  hipLaunchKernelGGL(topk_filter, dim3(tb.nchunks, rows), dim3(kFilterThreads), 0, stream, scores,
+                     counts, cand, T, kv_len, k, tb.nchunks);
+  int rc = check_launch("topk_filter");
+  if (rc) return rc;
+  hipLaunchKernelGGL(topk_select, dim3(rows), dim3(kThreads), 0, stream, scores, counts, cand, spill,
+                     idx, T, kv_len, k, tb.nchunks);
+  return check_launch("topk_select");
 }
 
 }  // namespace clsa

@@ -200,7 +200,8 @@ def score_rows(kind: str, B: int, T: int, L: int, seed: int, device="cpu") -> to
     kinds: "gauss" (N(0,1)), "ties" (integers in [0, 7]: huge tie classes),
     "zeros" (all +0/-0, mixed), "relu" (half exact zeros, signed zeros mixed,
     rest Gaussian), "needle" (N(0,1) with 1% of entries +8), "const" (all 3.5),
-    "desc" (strictly decreasing with position), "wide" (spans many octaves).
+    "desc" (strictly decreasing with position), "wide" (spans many octaves),
+    "strided" (every 64th position far above the rest).
     """
     g = _gen(seed, device)
     shape = (B, T, L)
@@ -224,6 +225,10 @@ def score_rows(kind: str, B: int, T: int, L: int, seed: int, device="cpu") -> to
         return torch.full(shape, 3.5, device=device)
     if kind == "desc":
         return (-torch.arange(L, device=device, dtype=torch.float32)).expand(shape).contiguous()
+    if kind == "strided":  # every 64th position far above the rest
+        x = torch.randn(shape, generator=g, device=device)
+        pos = torch.arange(L, device=device)
+        return torch.where((pos % 64 == 0).expand(shape), torch.full_like(x, 100.0), x)
     if kind == "wide":
         e = torch.randint(-60, 60, shape, generator=g, device=device).float()
         x = torch.randn(shape, generator=g, device=device)
