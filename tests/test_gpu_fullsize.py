@@ -1,0 +1,144 @@
+"""Parity at the workloads' full sizes, through the same clsa_decode_step call
+and launch configuration the benchmark times.
+
+The integer indexer recipe makes the index unique, so sampled index rows must
+match the oracle bit for bit; attention outputs of sampled (layer, batch or
+query) units must match the float64 oracle within tolerance. Where the
+oracle would take minutes (48 layers x 16 batch elements, a 2048-query chunk)
+it computes sampled units one by one: a query's index and attention depend
+only on that query, its indexer weights and the cache.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import token_sparse_attention_clsa_amd as clsa
+from token_sparse_attention_clsa_amd import inputs as inp
+
+from gpu_util import DEV, TOL_LSE, TOL_OUT, announce, lse_close, max_abs, out_f64, raw, require_gpu
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    require_gpu()
+
+
+class _Ref:
+    """Oracle results per sampled query, with host copies and indices memoised
+    (layers share caches and F layers' indices)."""
+
+    def __init__(self, wl, X):
+        self.wl, self.X = wl, X
+        self._raw, self._idx = {}, {}
+
+    def host(self, t, b):
+        key = (id(t), b)
+        if key not in self._raw:
+            self._raw[key] = raw(t[b:b + 1])
+        return self._raw[key]
+
+    def index(self, f, b, t):
+        wl, X = self.wl, self.X
+        if (f, b, t) not in self._idx:
+            vis = wl.kv_len - wl.T + t + 1
+            scores = oracle.index_score(raw(X.q_idx[f][b:b + 1, t:t + 1]), self.host(X.k_idx[f], b),
+                                        wl.idx_dtype, raw(X.w[f][b:b + 1, t:t + 1]), vis)
+            self._idx[(f, b, t)] = oracle.topk(scores, wl.k)
+        return self._idx[(f, b, t)]
+
+    def unit(self, layer, b, t):
+        """Index and attention of query (b, t) at `layer`, from that query alone."""
+        wl, X = self.wl, self.X
+        idx = self.index(wl.layer_src[layer], b, t)
+        vis = wl.kv_len - wl.T + t + 1
+        out, lse = oracle.sparse_attn(raw(X.q[layer][b:b + 1, t:t + 1]), self.host(X.k_cache[layer], b),
+                                      self.host(X.v_cache[layer], b), wl.dtype, idx, vis)
+        return idx[0, 0], out[0, 0], lse[0, 0]
+
+
+def _check_units(wl, X, st, units, ref=None):
+    ref = ref or _Ref(wl, X)
+    for layer, b, t in units:
+        idx, out, lse = ref.unit(layer, b, t)
+        if wl.layer_src[layer] == wl.f_layers[-1]:  # the index cache holds the last F layer's index
+            assert np.array_equal(st.idx[b, t].cpu().numpy(), idx), (layer, b, t)
+        assert max_abs(out_f64(st.out[layer][b, t]), out) <= TOL_OUT[wl.dtype], (layer, b, t)
+        lse_close(st.lse[layer][b, t].cpu().numpy(), lse, TOL_LSE[wl.dtype])
+    return ref
+
+
+def test_decode128k_full_step():
+    wl = inp.config("decode128k")
+    announce("full decode128k", wl.B, wl.kv_len, wl.n_layers)
+    X = inp.make(wl, "int", seed=11, device=DEV)
+    st = clsa.DecodeStep(wl.layer_src, X.q, X.k_cache, X.v_cache, X.q_idx, X.k_idx, X.w, wl.k,
+                         kv_len=wl.kv_len)
+    st.run()
+    torch.cuda.synchronize()
+    # every batch element's index, all 16 layers' outputs for two of them
+    ref = _check_units(wl, X, st, [(l, b, 0) for b in (0, 3) for l in range(wl.n_layers)])
+    _check_units(wl, X, st, [(15, b, 0) for b in (1, 2)], ref)
+    # the needles (keys x4) dominate the selection
+    needles = set(X.needles[0].tolist())
+    assert len(needles & set(st.idx[0, 0].tolist())) > 0.5 * len(needles)
+
+
+def test_decode32k_full_step_bf16_and_fp8_indexer():
+    for idx_dtype in (inp.BF16, inp.FP8_E4M3FN):
+        wl = inp.config("decode32k", idx_dtype=idx_dtype)
+        announce("full decode32k", inp.DTYPE_NAME[idx_dtype], wl.B, wl.kv_len)
+        X = inp.make(wl, "int", seed=12, device=DEV)
+        st = clsa.DecodeStep(wl.layer_src, X.q, X.k_cache, X.v_cache, X.q_idx, X.k_idx, X.w, wl.k)
+        st.run()
+        torch.cuda.synchronize()
+        _check_units(wl, X, st, [(l, b, 0) for b in (0, 7) for l in (0, 3, 7)] +
+                     [(7, b, 0) for b in range(1, 7)])
+
+
+def test_indexcache48_full_step():
+    wl = inp.config("indexcache48")
+    announce("full indexcache48", wl.B, wl.kv_len, wl.n_layers, "F layers", len(wl.f_layers))
+    try:
+        X = inp.make(wl, "int", seed=13, device=DEV)
+        note = "48 distinct per-layer caches"
+    except torch.cuda.OutOfMemoryError:
+        torch.cuda.empty_cache()
+        wl = inp.config("indexcache48", shared_kv=True)
+        X = inp.make(wl, "int", seed=13, device=DEV)
+        note = "one shared cache (per-layer caches did not fit)"
+    announce("indexcache48 inputs:", note)
+    st = clsa.DecodeStep(wl.layer_src, X.q, X.k_cache, X.v_cache, X.q_idx, X.k_idx, X.w, wl.k)
+    st.run()
+    torch.cuda.synchronize()
+    # layers served by F layers 0, 20 and 44, at both ends of the batch
+    _check_units(wl, X, st, [(l, b, 0) for b in (0, 15) for l in (0, 3, 21, 44, 47)])
+    del X, st
+    torch.cuda.empty_cache()
+
+
+def test_prefill2k_full_chunk():
+    wl = inp.config("prefill2k")
+    announce("full prefill2k", wl.T, wl.kv_len, wl.k)
+    X = inp.make(wl, "int", seed=14, device=DEV)
+    st = clsa.DecodeStep(wl.layer_src, X.q, X.k_cache, X.v_cache, X.q_idx, X.k_idx, X.w, wl.k)
+    st.run()
+    torch.cuda.synchronize()
+    _check_units(wl, X, st, [(0, 0, t) for t in (0, 1, 777, 1500, 2046, 2047)])
+    # causality: no query selects a position it does not see
+    idx = st.idx[0].cpu().numpy()
+    vis = wl.kv_len - wl.T + np.arange(wl.T) + 1
+    assert np.all(idx < vis[:, None])
+    assert np.all(idx >= 0)  # every query sees more than k positions
+
+
+def test_topk_at_maximum_row_length():
+    L, k = 4 * 1024 * 1024, 2048
+    announce("topk max row", L, k)
+    s = inp.score_rows("needle", 1, 1, L, 15, DEV)
+    idx = clsa.topk(s, k)
+    torch.cuda.synchronize()
+    assert np.array_equal(idx.cpu().numpy(), oracle.topk(s.double().cpu().numpy(), k))
