@@ -27,6 +27,25 @@ import sys
 import time
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E
+ROOT = os.path.dirname(os.path.abspath(__file__))
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "sparse_attn_decode128k_traffic.txt")
+ATTN_SOURCE = os.path.join(ROOT, "token_sparse_attention_clsa_amd", "csrc", "sparse_attn.hip")
+
+
+def measured_traffic(config_name):
+    """HBM bytes per attention call from the committed rocprofv3 counter summary
+    (FETCH_SIZE + WRITE_SIZE, calibrated on a copy kernel), if that summary was
+    taken on the current kernel source and this workload; else None."""
+    import hashlib
+    try:
+        fields = dict(line.split("=", 1) for line in open(TRAFFIC_FILE).read().split("\n")
+                      if "=" in line and not line.startswith("#"))
+    except OSError:
+        return None
+    sha = hashlib.sha256(open(ATTN_SOURCE, "rb").read()).hexdigest()
+    if fields.get("source_sha256", "").strip() != sha or fields.get("workload", "").strip() != config_name:
+        return None
+    return float(fields["bytes_per_call"])
 
 
 def algorithmic_bytes(wl):
@@ -91,6 +110,8 @@ def main():
     ap.add_argument("--variant", default="gauss", choices=["gauss", "int"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="run 3 plain device copies of this many MiB first (counter calibration)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -111,6 +132,14 @@ def main():
     wl = inp.config(args.config)
     print(f"[bench] workload {wl.name}: B={wl.B} T={wl.T} kv_len={wl.kv_len} layers={wl.n_layers} "
           f"F={len(wl.f_layers)} k={wl.k}", file=sys.stderr, flush=True)
+    if args.calib_copy_mib:
+        src = torch.empty(args.calib_copy_mib << 18, dtype=torch.float32, device="cuda").fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     X = inp.make(wl, args.variant, seed=7, device="cuda")
     n = wl.n_layers
     K, W = args.steps, args.warmup
@@ -204,7 +233,7 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": attn_gbs / HBM_PEAK_GBS,
-            "traffic": None,
+            "traffic": measured_traffic(wl.name),
             "bytes_per_launch": alg["sparse_attn"],
             "avg_launch_us": us_attn,
         },
