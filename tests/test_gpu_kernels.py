@@ -43,6 +43,13 @@ IDX_CASES = [
     (inp.BF16, 1, 5, 32, 128, 70, 80, 4),
     (inp.FP8_E4M3FN, 2, 1, 64, 128, 5000, 5000, 4),
     (inp.FP8_E4M3FN, 1, 2, 32, 64, 777, 800, 4),
+    # T >= 8: the multi-query (LDS-tiled) form
+    (inp.BF16, 1, 8, 64, 128, 3000, 3000, 4),
+    (inp.BF16, 2, 19, 32, 64, 1000, 1100, 4),    # a partial group of queries
+    (inp.FP8_E4M3FN, 1, 16, 64, 128, 2049, 2049, 4),
+    (inp.FP8_E4M3FN, 2, 9, 48, 64, 600, 640, 4),
+    (inp.BF16, 1, 64, 16, 128, 700, 700, 4),     # kv_len close to T: short visible rows
+    (inp.BF16, 1, 40, 64, 128, 40, 40, 4),       # T == kv_len: query 0 sees one key
 ]
 
 

@@ -133,6 +133,131 @@ __global__ __launch_bounds__(kIdxThreads) void idx_score_mfma(
   }
 }
 
+// Multi-query form (chunked prefill): a workgroup of kQB waves takes kQB
+// consecutive queries of one batch element (wave w = query t0 + w, its heads
+// in VGPRs as above) and a range of keys. Key tiles of kKT keys are copied
+// from global memory into LDS once per workgroup (double-buffered, rows padded
+// to D_I*elt + 16 bytes so the 16 rows one B-fragment read touches fall in
+// distinct banks) and every wave runs its MFMAs on the shared tile, so each
+// key row leaves L2 once per kQB queries instead of once per query.
+// grid (key_splits, B * ceil(T / kQB)), block kQB * 64.
+constexpr int kQB = 8;
+constexpr int kKT = 64;
+
+template <int DT, int DI, int HI>
+__global__ __launch_bounds__(kQB * kWave) void idx_score_multi(
+    const uint8_t* __restrict__ q_idx, const uint8_t* __restrict__ k_idx,
+    const float* __restrict__ w, float* __restrict__ scores, int T, int kv_len, int L_cap,
+    int keys_per_split) {
+  using E = IdxElem<DT>;
+  constexpr int NS = DI / 32;
+  constexpr int NH = HI / 16;
+  constexpr int ROWB = DI * E::bytes;        // bytes of one key row
+  constexpr int PITCH = ROWB + 16;           // padded LDS row
+  constexpr int CHUNKS = ROWB / 16;          // 16-byte chunks per row
+  constexpr int TILE_CHUNKS = kKT * CHUNKS;  // per tile
+  __shared__ __attribute__((aligned(16))) uint8_t tile[2][kKT * PITCH];
+
+  const int lane = threadIdx.x % kWave;
+  const int wave = threadIdx.x / kWave;
+  const int col = lane % 16, grp = lane / 16;
+  const int groups_per_b = (T + kQB - 1) / kQB;
+  const int b = blockIdx.y / groups_per_b;
+  const int t = (blockIdx.y % groups_per_b) * kQB + wave;
+  const bool active = t < T;
+  const int tt = active ? t : T - 1;  // inactive waves mirror a valid query, store nothing
+  const int bt = b * T + tt;
+  const int vis = kv_len - T + tt + 1;
+  const int vis_max = kv_len - T + min(T - 1, (blockIdx.y % groups_per_b) * kQB + kQB - 1) + 1;
+
+  typename E::frag a[NH][NS];
+  const uint8_t* qrow = q_idx + (size_t)bt * HI * DI * E::bytes;
+#pragma unroll
+  for (int ht = 0; ht < NH; ht++)
+#pragma unroll
+    for (int s = 0; s < NS; s++)
+      a[ht][s] = E::load(qrow + ((size_t)(ht * 16 + col) * DI + grp * (DI / 4) + 8 * s) * E::bytes);
+  float wv[NH][4];
+#pragma unroll
+  for (int ht = 0; ht < NH; ht++)
+#pragma unroll
+    for (int r = 0; r < 4; r++) wv[ht][r] = w[(size_t)bt * HI + ht * 16 + 4 * grp + r];
+
+  const uint8_t* kbase = k_idx + (size_t)b * L_cap * ROWB;
+  float* srow = scores + (size_t)bt * kv_len;
+  const int k0 = blockIdx.x * keys_per_split;
+  const int k1 = min(k0 + keys_per_split, kv_len);
+  const int kend = min(k1, vis_max);  // keys any query of the group sees
+
+  // Global -> registers -> LDS: each thread moves chunks c0 and c1 (16 bytes each).
+  static_assert(TILE_CHUNKS <= 2 * kQB * kWave, "two staged chunks per thread");
+  const int c0 = threadIdx.x, c1 = threadIdx.x + kQB * kWave;
+  uint4 st0 = {0, 0, 0, 0}, st1 = {0, 0, 0, 0};
+#define CLSA_FETCH(key0)                                                                      \
+  {                                                                                           \
+    if (c0 < TILE_CHUNKS)                                                                     \
+      st0 = *reinterpret_cast<const uint4*>(                                                  \
+          kbase + (size_t)min((key0) + c0 / CHUNKS, kv_len - 1) * ROWB + (c0 % CHUNKS) * 16); \
+    if (c1 < TILE_CHUNKS)                                                                     \
+      st1 = *reinterpret_cast<const uint4*>(                                                  \
+          kbase + (size_t)min((key0) + c1 / CHUNKS, kv_len - 1) * ROWB + (c1 % CHUNKS) * 16); \
+  }
+#define CLSA_COMMIT(buf)                                                                           \
+  {                                                                                                \
+    if (c0 < TILE_CHUNKS)                                                                          \
+      *reinterpret_cast<uint4*>(&tile[buf][(c0 / CHUNKS) * PITCH + (c0 % CHUNKS) * 16]) = st0;      \
+    if (c1 < TILE_CHUNKS)                                                                          \
+      *reinterpret_cast<uint4*>(&tile[buf][(c1 / CHUNKS) * PITCH + (c1 % CHUNKS) * 16]) = st1;      \
+  }
+
+  // Keys past the group's visible range are written as -inf without compute.
+  for (int key = max(k0, kend) + threadIdx.x % kWave; key < k1; key += kWave)
+    if (active) srow[key] = -INFINITY;
+  if (k0 >= kend) return;  // uniform over the workgroup
+
+  CLSA_FETCH(k0)
+  CLSA_COMMIT(0)
+  __syncthreads();
+  int buf = 0;
+  for (int base = k0; base < kend; base += kKT) {  // uniform over the workgroup
+    const bool more = base + kKT < kend;
+    if (more) {
+      CLSA_FETCH(base + kKT)  // in flight while this tile is computed
+    }
+    float res = 0.f;
+#pragma unroll
+    for (int j = 0; j < kKT / 16; j++) {
+      f32x4 acc[NH];
+#pragma unroll
+      for (int ht = 0; ht < NH; ht++) acc[ht] = f32x4{0.f, 0.f, 0.f, 0.f};
+      const uint8_t* rowp = &tile[buf][(j * 16 + col) * PITCH + grp * (ROWB / 4)];
+#pragma unroll
+      for (int s = 0; s < NS; s++) {
+        const typename E::frag bf = E::load(rowp + 8 * s * E::bytes);
+#pragma unroll
+        for (int ht = 0; ht < NH; ht++) acc[ht] = E::mfma(a[ht][s], bf, acc[ht]);
+      }
+      float v = 0.f;
+#pragma unroll
+      for (int ht = 0; ht < NH; ht++)
+#pragma unroll
+        for (int r = 0; r < 4; r++) v += wv[ht][r] * fmaxf(acc[ht][r], 0.f);
+      v += __shfl_xor(v, 16, kWave);
+      v += __shfl_xor(v, 32, kWave);
+      if (grp == j) res = v;
+    }
+    const int key_out = base + grp * 16 + col;
+    if (active && key_out < k1) srow[key_out] = key_out < vis ? res : -INFINITY;
+    if (more) {
+      CLSA_COMMIT(buf ^ 1)
+      __syncthreads();  // next tile visible; everyone is done with this one
+      buf ^= 1;
+    }
+  }
+#undef CLSA_FETCH
+#undef CLSA_COMMIT
+}
+
 // Float32 indexer (small head counts): one thread per key, the query's heads
 // and weights staged in LDS. grid: (ceil(kv_len/256), B*T), block 256,
 // dynamic LDS (H*D + H) floats.
@@ -168,6 +293,22 @@ __global__ __launch_bounds__(256) void idx_score_f32(const float* __restrict__ q
 template <int DT, int DI, int HI>
 int launch_mfma(const void* q, const void* k, const float* w, float* scores, int B, int T,
                 int kv_len, int L_cap, hipStream_t stream) {
+  if (T >= kQB) {
+    // Enough workgroups to cover the chip: split the keys when query groups are few.
+    const int groups = B * ((T + kQB - 1) / kQB);
+    int splits = (512 + groups - 1) / groups;
+    const int max_splits = (kv_len + kKT * 8 - 1) / (kKT * 8);  // at least 8 tiles per split
+    if (splits > max_splits) splits = max_splits;
+    if (splits < 1) splits = 1;
+    int keys = (kv_len + splits - 1) / splits;
+    keys = (keys + kKT - 1) / kKT * kKT;
+    splits = (kv_len + keys - 1) / keys;
+    dim3 grid(splits, groups);
+    hipLaunchKernelGGL((idx_score_multi<DT, DI, HI>), grid, dim3(kQB * kWave), 0, stream,
+                       static_cast<const uint8_t*>(q), static_cast<const uint8_t*>(k), w, scores, T,
+                       kv_len, L_cap, keys);
+    return check_launch("idx_score_multi");
+  }
   const int keys_per_wg = 1024;
   dim3 grid((kv_len + keys_per_wg - 1) / keys_per_wg, B * T);
   hipLaunchKernelGGL((idx_score_mfma<DT, DI, HI>), grid, dim3(kIdxThreads), 0, stream,
