@@ -202,6 +202,32 @@ def main():
     step_bytes = len(wl.f_layers) * (alg["index_score"] + alg["topk"]) + n * alg["sparse_attn"]
     f_layers = wl.f_layers
 
+    comparator = None
+    if wl.T > 1:
+        # Block-union comparator on the same chunk: union table of the step's
+        # index (64-token blocks), then dense attention over the table.
+        block = 64
+        indptr, indices = clsa.block_union_build(idx, wl.kv_len, block, wl.Hkv)
+        torch.cuda.synchronize()
+        n_blocks = int(indptr[1].item() - indptr[0].item())
+        out_b = torch.empty_like(X.q[0])
+        lse_b = torch.empty((wl.B, wl.T, wl.Hq), dtype=torch.float32, device="cuda")
+        us_union = per_launch_us(lambda i: clsa.block_union_build(idx, wl.kv_len, block, wl.Hkv))
+        us_paged = per_launch_us(lambda i: clsa.block_paged_attn(X.q[0], X.k_cache[0], X.v_cache[0], indptr,
+                                                                 indices, block, kv_len=wl.kv_len, out=out_b,
+                                                                 lse=lse_b))
+        pos = min(n_blocks * block, wl.kv_len)
+        vis_sum = sum(min(pos, wl.kv_len - wl.T + t + 1) for t in range(wl.T))  # upper bound of keys seen
+        flops = 4.0 * wl.B * wl.Hq * wl.D * vis_sum
+        comparator = {
+            "block": block,
+            "union_blocks_per_group": n_blocks,
+            "block_union_build_us": us_union,
+            "block_paged_attn_us": us_paged,
+            "block_paged_attn_tflops_upper": flops / (us_paged * 1e-6) / 1e12,
+            "sparse_attn_us": us_attn,
+        }
+
     tokens_per_step = wl.B * wl.T
     result = {
         "metric": "decode tokens/sec + achieved HBM GB/s, sparse-attn step @128K ctx, top-k 2048",
@@ -245,6 +271,8 @@ def main():
         },
         "ms_per_step_events": ms_per_step_events,
     }
+    if comparator is not None:
+        result["block_union_comparator"] = comparator
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle) ...", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(wl, X, args.cpu_budget)

@@ -46,6 +46,9 @@ def test_block_union_table_matches_oracle(B, T, L, k, block, Hkv):
     (1, 8, 1500, 64, 64, 32, 8),
     (2, 3, 700, 50, 16, 8, 2),
     (1, 4, 500, 500, 64, 8, 8),    # full union: dense causal attention
+    (1, 40, 3000, 64, 64, 32, 8),  # two query tiles, ~45 KV tiles, a partial last block
+    (2, 70, 1000, 20, 16, 16, 16), # G = 1, block 16, tiles spanning 4 blocks
+    (1, 9, 2000, 30, 48, 64, 8),   # G = 8, block size not dividing the 64-position tile
 ])
 def test_block_paged_attention_matches_oracle(B, T, L, k, block, Hq, Hkv):
     announce("block_paged_attn", B, T, L, k, block, Hq, Hkv)

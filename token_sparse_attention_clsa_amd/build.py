@@ -19,7 +19,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libclsa.so")
-SOURCES = ["api.cpp", "index_score.hip", "topk.hip", "sparse_attn.hip", "block_union.hip"]
+SOURCES = ["api.cpp", "index_score.hip", "topk.hip", "sparse_attn.hip", "block_union.hip",
+           "block_attn.hip"]
 ARCH = "gfx950"
 
 

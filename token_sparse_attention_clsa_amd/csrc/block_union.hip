@@ -16,10 +16,10 @@
 
 namespace clsa {
 
-int launch_block_attn_gather(const void* q, const void* kc, const void* vc, int dtype,
-                             const int32_t* kv_indptr, const int32_t* kv_indices, int block,
-                             void* out, float* lse, int B, int T, int Hq, int Hkv, int D,
-                             int kv_len, int L_cap, float scale, hipStream_t stream);
+int launch_block_attn_mfma(const void* q, const void* kc, const void* vc,
+                           const int32_t* kv_indptr, const int32_t* kv_indices, int block,
+                           void* out, float* lse, int B, int T, int Hq, int Hkv, int D, int kv_len,
+                           int L_cap, float scale, hipStream_t stream);
 
 namespace {
 
@@ -102,8 +102,9 @@ int launch_block_paged_attn(const void* q, const void* kc, const void* vc, int d
                             const int32_t* kv_indptr, const int32_t* kv_indices, int block,
                             void* out, float* lse, int B, int T, int Hq, int Hkv, int D,
                             int kv_len, int L_cap, float scale, hipStream_t stream) {
-  return launch_block_attn_gather(q, kc, vc, dtype, kv_indptr, kv_indices, block, out, lse, B, T,
-                                  Hq, Hkv, D, kv_len, L_cap, scale, stream);
+  (void)dtype;  // bf16 only (checked by the caller)
+  return launch_block_attn_mfma(q, kc, vc, kv_indptr, kv_indices, block, out, lse, B, T, Hq, Hkv, D,
+                                kv_len, L_cap, scale, stream);
 }
 
 }  // namespace clsa

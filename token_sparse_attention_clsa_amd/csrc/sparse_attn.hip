@@ -347,100 +347,6 @@ __global__ __launch_bounds__(kD) void attn_combine_kernel(const float* __restric
   if (d == 0 && lse) lse[head] = L > 0.f ? (M + log2f(L)) * kLn2 : -INFINITY;
 }
 
-// Block-table gather path (dense attention over every position of the
-// listed blocks): one workgroup per (query, KV head), 4 waves, no split.
-struct BlockSrc {
-  const int32_t* indptr;
-  const int32_t* indices;
-  int block, T, Hkv;
-};
-
-template <int DT, int G>
-__global__ __launch_bounds__(256) void block_gather_kernel(
-    const char* __restrict__ q, const char* __restrict__ kc, const char* __restrict__ vc,
-    BlockSrc src, void* __restrict__ out, float* __restrict__ lse, int T, int Hkv, int kv_len,
-    int L_cap, float c_log2) {
-  using E = AttnElem<DT>;
-  constexpr int ROW = kD * E::bytes;
-  const int lane = threadIdx.x % kWave;
-  const int wave = threadIdx.x / kWave;
-  const int sub = lane % 16, rg = lane / 16;
-  const int g = blockIdx.y, bt = blockIdx.z;
-  const int b = bt / T, t = bt % T;
-  const int vis = kv_len - T + t + 1;
-  const int Hq = Hkv * G;
-  const int u = b * Hkv + g;
-  const int32_t* list = src.indices + src.indptr[u];
-  const int n = (src.indptr[u + 1] - src.indptr[u]) * src.block;
-
-  typename E::Frag qf[G];
-#pragma unroll
-  for (int h = 0; h < G; h++)
-    qf[h] = E::load(q + (((size_t)bt * Hq + g * G + h) * kD + 8 * sub) * E::bytes);
-  HeadState<G> st;
-  st.init();
-  const char* kb = kc + ((size_t)b * L_cap * Hkv + g) * ROW + 8 * sub * E::bytes;
-  const char* vb = vc + ((size_t)b * L_cap * Hkv + g) * ROW + 8 * sub * E::bytes;
-  const size_t tok = (size_t)Hkv * ROW;
-  for (int wb = wave * 16; wb < n; wb += 64) {  // wave-uniform
-    int pos[4];
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-      const int r = wb + rg * 4 + i;
-      const int p = r < n ? list[r / src.block] * src.block + r % src.block : -1;
-      pos[i] = (p >= 0 && p < vis) ? p : -1;
-    }
-    typename E::Frag kf[4], vf[4];
-#pragma unroll
-    for (int i = 0; i < 4; i++) kf[i] = E::load(kb + (size_t)max(pos[i], 0) * tok);
-#pragma unroll
-    for (int i = 0; i < 4; i++) vf[i] = E::load(vb + (size_t)max(pos[i], 0) * tok);
-    float uu[4][G];
-#pragma unroll
-    for (int i = 0; i < 4; i++)
-#pragma unroll
-      for (int h = 0; h < G; h++) {
-        const float sc = dpp_sum16(E::dot(qf[h], kf[i]));
-        uu[i][h] = pos[i] >= 0 ? sc * c_log2 : -INFINITY;
-      }
-    float v[4][8];
-#pragma unroll
-    for (int i = 0; i < 4; i++) E::to_f32(vf[i], v[i]);
-    st.update(uu, v);
-  }
-  st.merge_xor(16);
-  st.merge_xor(32);
-  __shared__ float sh[4][G][kD + 2];
-  if (lane < 16) {
-#pragma unroll
-    for (int h = 0; h < G; h++) {
-#pragma unroll
-      for (int e = 0; e < 8; e++) sh[wave][h][2 + 8 * sub + e] = st.o[h][e];
-      if (sub == 0) {
-        sh[wave][h][0] = st.m[h];
-        sh[wave][h][1] = st.l[h];
-      }
-    }
-  }
-  __syncthreads();
-  for (int item = threadIdx.x; item < G * kD; item += blockDim.x) {
-    const int h = item / kD, d = item % kD;
-    float M = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < 4; w++) M = fmaxf(M, sh[w][h][0]);
-    float L = 0.f, O = 0.f;
-#pragma unroll
-    for (int w = 0; w < 4; w++) {
-      const float a = rescale(sh[w][h][0], M);
-      L += sh[w][h][1] * a;
-      O += sh[w][h][2 + d] * a;
-    }
-    const size_t head = (size_t)bt * Hq + g * G + h;
-    E::store(out, head * kD + d, L > 0.f ? O / L : 0.f);
-    if (d == 0 && lse) lse[head] = L > 0.f ? (M + log2f(L)) * kLn2 : -INFINITY;
-  }
-}
-
 // Waves per workgroup: the largest divisor of Hkv that is at most kMaxWaves.
 int waves_for(int Hkv) {
   for (int w = kMaxWaves; w > 1; w--)
@@ -476,23 +382,6 @@ int dispatch_index_path(int G, const void* q, const void* kc, const void* vc, co
     case 8: return launch_index_path<DT, 8>(q, kc, vc, idx, k, out, lse, B, T, Hkv, kv_len, L_cap, c_log2, sp, part, s);
   }
   return set_error(CLSA_ERR_UNSUPPORTED, "sparse_attn: Hq/Hkv=%d", G);
-}
-
-template <int DT>
-int dispatch_block_path(int G, const void* q, const void* kc, const void* vc, BlockSrc src,
-                        void* out, float* lse, int B, int T, int Hkv, int kv_len, int L_cap,
-                        float c_log2, hipStream_t s) {
-  dim3 grid(1, Hkv, B * T);
-  const char *qq = static_cast<const char*>(q), *kk = static_cast<const char*>(kc),
-             *vv = static_cast<const char*>(vc);
-  switch (G) {
-    case 1: hipLaunchKernelGGL((block_gather_kernel<DT, 1>), grid, dim3(256), 0, s, qq, kk, vv, src, out, lse, T, Hkv, kv_len, L_cap, c_log2); break;
-    case 2: hipLaunchKernelGGL((block_gather_kernel<DT, 2>), grid, dim3(256), 0, s, qq, kk, vv, src, out, lse, T, Hkv, kv_len, L_cap, c_log2); break;
-    case 4: hipLaunchKernelGGL((block_gather_kernel<DT, 4>), grid, dim3(256), 0, s, qq, kk, vv, src, out, lse, T, Hkv, kv_len, L_cap, c_log2); break;
-    case 8: hipLaunchKernelGGL((block_gather_kernel<DT, 8>), grid, dim3(256), 0, s, qq, kk, vv, src, out, lse, T, Hkv, kv_len, L_cap, c_log2); break;
-    default: return set_error(CLSA_ERR_UNSUPPORTED, "block attention: Hq/Hkv=%d", G);
-  }
-  return check_launch("block_gather");
 }
 
 }  // namespace
@@ -540,20 +429,6 @@ int launch_sparse_attn(const void* q, const void* kc, const void* vc, int dtype,
                                           c_log2, sp, partials, stream);
   return dispatch_index_path<CLSA_F32>(G, q, kc, vc, idx, k, out, lse, B, T, Hkv, kv_len, L_cap,
                                        c_log2, sp, partials, stream);
-}
-
-int launch_block_attn_gather(const void* q, const void* kc, const void* vc, int dtype,
-                             const int32_t* kv_indptr, const int32_t* kv_indices, int block,
-                             void* out, float* lse, int B, int T, int Hq, int Hkv, int D,
-                             int kv_len, int L_cap, float scale, hipStream_t stream) {
-  const float c_log2 = (scale > 0.f ? scale : 1.f / sqrtf((float)D)) * kLog2e;
-  const int G = Hq / Hkv;
-  BlockSrc src{kv_indptr, kv_indices, block, T, Hkv};
-  if (dtype == CLSA_BF16)
-    return dispatch_block_path<CLSA_BF16>(G, q, kc, vc, src, out, lse, B, T, Hkv, kv_len, L_cap,
-                                          c_log2, stream);
-  return dispatch_block_path<CLSA_F32>(G, q, kc, vc, src, out, lse, B, T, Hkv, kv_len, L_cap,
-                                       c_log2, stream);
 }
 
 }  // namespace clsa
