@@ -110,6 +110,7 @@ def main():
     ap.add_argument("--variant", default="gauss", choices=["gauss", "int"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--no-graph", action="store_true", help="skip the HIP-graph replay timing")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="run 3 plain device copies of this many MiB first (counter calibration)")
     args = ap.parse_args()
@@ -164,6 +165,29 @@ def main():
     ms_per_step_events = e0.elapsed_time(e1) / K
     print(f"[bench] timed {K} steps: {ms_per_step * 1e3:.1f} us/step (events {ms_per_step_events * 1e3:.1f})",
           file=sys.stderr, flush=True)
+
+    # The same step captured once in a HIP graph and replayed K times (one
+    # launch per step instead of one per kernel; the work is identical).
+    graph_ms = None
+    if not args.no_graph:
+        g = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step.run()  # the step issues no allocations and no memset nodes
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g):
+            step.run()
+        for _ in range(W):
+            g.replay()
+        torch.cuda.synchronize()
+        t2 = time.perf_counter()
+        for _ in range(K):
+            g.replay()
+        torch.cuda.synchronize()
+        graph_ms = (time.perf_counter() - t2) * 1e3 / K
+        print(f"[bench] graph replay: {graph_ms * 1e3:.1f} us/step", file=sys.stderr, flush=True)
 
     # Per-kernel averages: R back-to-back launches of one entry point on the
     # stream, bracketed by one event pair (no event between launches, which
@@ -270,6 +294,7 @@ def main():
             "index_score_gbs": alg["index_score"] / (us_index * 1e-6) / 1e9,
         },
         "ms_per_step_events": ms_per_step_events,
+        "ms_per_step_graph_replay": graph_ms,
     }
     if comparator is not None:
         result["block_union_comparator"] = comparator

@@ -114,20 +114,14 @@ struct AttnElem<CLSA_F32> {
 };
 
 // Sum over each row of 16 lanes, result in all 16 lanes (DPP butterfly:
-// swap neighbours, swap pairs, mirror within 8, mirror within 16).
+// swap neighbours, swap pairs, mirror within 8, mirror within 16). Every
+// source lane exists for these patterns, so bound_ctrl changes nothing; it
+// lets the compiler fold each step into one v_add_f32_dpp.
 __device__ __forceinline__ float dpp_sum16(float v) {
-  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));
-  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false));
-  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, false));
-  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x140, 0xF, 0xF, false));
-  return v;
-}
-
-__device__ __forceinline__ float sum16_shfl(float v) {
-  v += __shfl_xor(v, 1, kWave);
-  v += __shfl_xor(v, 2, kWave);
-  v += __shfl_xor(v, 4, kWave);
-  v += __shfl_xor(v, 8, kWave);
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, true));
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, true));
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, true));
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x140, 0xF, 0xF, true));
   return v;
 }
 
@@ -301,6 +295,228 @@ __global__ __launch_bounds__(kWave * kMaxWaves) void attn_split_kernel(
   }
 }
 
+// bf16 split kernel on matrix cores (same grid, work split and outputs as
+// attn_split_kernel). One wave per KV head g; entries go in steps of 32,
+// as two tiles of 16 keys. Lane l = 16 * grp + col.
+//  - Scores: S^T[key, h] = K[key, :] . q[h, :] with v_mfma_f32_16x16x32_bf16.
+//    A = 16 gathered K rows (lane: key col, d = 8 * grp + 32 * ks + 0..7),
+//    B = the G query heads (lane: head col, zero for col >= G). Lane
+//    (grp, col) receives head col for keys 4 * grp + r of each tile.
+//  - Softmax: one running max per head shared by the four lane groups (a
+//    cross-group max through v_permlane16/32_swap), so the per-group partial
+//    sums add without rescaling; each exp is taken once.
+//  - Output: O^T[d, h] += V^T[d, key] . P^T[key, h], P rounded to bf16. The
+//    lane's 8 probabilities are already the B operand (k slot x = 4 * tile +
+//    r of lane group grp is key 16 * tile + 4 * grp + r). V^T goes through a
+//    per-wave LDS tile: each lane gathers 16-byte V row pieces (same keys as
+//    its probabilities, d = 8 * col + 0..7) and writes them transposed; the
+//    A fragments are read back as two 8-byte pieces. Rows and 8-byte chunks of
+//    the tile are XOR-swizzled so that both the writes (16 lanes: one key
+//    group, 16 d-slices) and the reads (16 lanes: 16 consecutive d) touch 16
+//    distinct 8-byte bank slots.
+//  Lane (grp, col) ends with O^T[16 * j + 4 * grp + s][col], j = 0..7, s = 0..3.
+constexpr int kVtBytes = kD * 64;  // per-wave V^T tile: 128 d-rows x 32 keys x bf16
+
+// Byte offset of the 8-byte chunk c8 (keys 4 * c8 .. 4 * c8 + 3) of d-row d.
+__host__ __device__ constexpr int vt_addr(int d, int c8) {
+  const int row = d ^ ((d >> 4) & 1);
+  const int h = (((d >> 1) ^ (d >> 5)) & 1) | ((((d >> 2) ^ (d >> 6)) & 1) << 1) | (((d >> 3) & 1) << 2);
+  return row * 64 + 8 * (c8 ^ h);
+}
+
+__device__ __forceinline__ float xgroup_max(float v) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float xgroup_sum(float v) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+// Low or high bf16 halves of four words packed as 4 x bf16 (8 bytes).
+__device__ __forceinline__ uint2 pack4(uint32_t a, uint32_t b, uint32_t c, uint32_t d, bool hi) {
+  const uint32_t sel = hi ? 0x07060302u : 0x05040100u;
+  return make_uint2(__builtin_amdgcn_perm(b, a, sel), __builtin_amdgcn_perm(d, c, sel));
+}
+// Two floats to bf16 (round to nearest even; v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+  const bf16x2 v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+template <int G>
+__global__ __launch_bounds__(kWave * kMaxWaves) void attn_split_mfma(
+    const char* __restrict__ q, const char* __restrict__ kc, const char* __restrict__ vc,
+    const int32_t* __restrict__ idx, int k, void* __restrict__ out, float* __restrict__ lse,
+    int T, int Hkv, int kv_len, int L_cap, float c_log2, int rows_per_split,
+    float* __restrict__ partials) {
+  constexpr int ROW = kD * 2;
+  __shared__ int s_pos[kTileRows];
+  __shared__ __attribute__((aligned(16))) char s_vt[kMaxWaves * kVtBytes];
+  const int lane = threadIdx.x % kWave;
+  const int wave = threadIdx.x / kWave;
+  const int nw = blockDim.x / kWave;
+  const int col = lane % 16;
+  const int grp = lane / 16;
+  const int split = blockIdx.x, S = gridDim.x;
+  const int bt = blockIdx.y;
+  const int g = blockIdx.z * nw + wave;
+  const int b = bt / T, t = bt % T;
+  const int vis = kv_len - T + t + 1;
+  const int Hq = Hkv * G;
+  const int r0 = split * rows_per_split;
+  const int r1 = min(k, r0 + rows_per_split);
+  const int32_t* irow = idx + (size_t)bt * k;
+  char* vt = s_vt + wave * kVtBytes;
+
+  bf16x8 qf[4];
+#pragma unroll
+  for (int ks = 0; ks < 4; ks++) {
+    uint4 u = {0u, 0u, 0u, 0u};
+    if (col < G)
+      u = *reinterpret_cast<const uint4*>(q + (((size_t)bt * Hq + g * G + col) * kD + 8 * grp + 32 * ks) * 2);
+    qf[ks] = __builtin_bit_cast(bf16x8, u);
+  }
+  f32x4 o[8];
+#pragma unroll
+  for (int j = 0; j < 8; j++) o[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m = -INFINITY, l = 0.f;  // head col; m shared by the lane groups, l per group
+
+  // LDS offsets: the write addresses depend on the lane and on (e, tile)
+  // only through XOR with a constant, likewise the reads on (j, tile).
+  const int wbase = vt_addr(8 * col, grp);
+  const int rbase = vt_addr(col, grp);
+
+  const char* kb = kc + ((size_t)b * L_cap * Hkv + g) * ROW + (8 * grp) * 2;
+  const char* vb = vc + ((size_t)b * L_cap * Hkv + g) * ROW + 16 * col;
+  const size_t tok = (size_t)Hkv * ROW;
+
+  for (int t0 = r0; t0 < r1; t0 += kTileRows) {  // uniform over the workgroup
+    const int n = min(kTileRows, r1 - t0);
+    __syncthreads();
+    for (int i = threadIdx.x; i < n; i += blockDim.x) {
+      const int p = irow[t0 + i];
+      s_pos[i] = (p >= 0 && p < vis) ? p : -1;
+    }
+    __syncthreads();
+    for (int base = 0; base < n; base += 32) {  // uniform over the wave
+      int kp[2], vp[2][4];
+#pragma unroll
+      for (int tt = 0; tt < 2; tt++) {
+        const int rk = base + 16 * tt + col;
+        kp[tt] = rk < n ? s_pos[rk] : -1;
+#pragma unroll
+        for (int r = 0; r < 4; r++) {
+          const int rv = base + 16 * tt + 4 * grp + r;
+          vp[tt][r] = rv < n ? s_pos[rv] : -1;
+        }
+      }
+      bf16x8 kf[2][4];
+      uint4 vf[2][4];
+#pragma unroll
+      for (int tt = 0; tt < 2; tt++)
+#pragma unroll
+        for (int ks = 0; ks < 4; ks++)
+          kf[tt][ks] = __builtin_bit_cast(
+              bf16x8, *reinterpret_cast<const uint4*>(kb + (size_t)max(kp[tt], 0) * tok + 64 * ks));
+#pragma unroll
+      for (int tt = 0; tt < 2; tt++)
+#pragma unroll
+        for (int r = 0; r < 4; r++)
+          vf[tt][r] = *reinterpret_cast<const uint4*>(vb + (size_t)max(vp[tt][r], 0) * tok);
+      f32x4 sc[2];
+#pragma unroll
+      for (int tt = 0; tt < 2; tt++) {
+        sc[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < 4; ks++) sc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[tt][ks], qf[ks], sc[tt], 0, 0, 0);
+      }
+      // Stage V^T while the scores are in flight.
+#pragma unroll
+      for (int tt = 0; tt < 2; tt++) {
+        const uint32_t* w0 = reinterpret_cast<const uint32_t*>(&vf[tt][0]);
+        const uint32_t* w1 = reinterpret_cast<const uint32_t*>(&vf[tt][1]);
+        const uint32_t* w2 = reinterpret_cast<const uint32_t*>(&vf[tt][2]);
+        const uint32_t* w3 = reinterpret_cast<const uint32_t*>(&vf[tt][3]);
+#pragma unroll
+        for (int e = 0; e < 8; e++) {
+          const int off = wbase ^ (vt_addr(e, 4 * tt) ^ vt_addr(0, 0));
+          *reinterpret_cast<uint2*>(vt + off) =
+              pack4(w0[e / 2], w1[e / 2], w2[e / 2], w3[e / 2], e & 1);
+        }
+      }
+      // Online softmax of head col over the 32 keys.
+      float u[2][4];
+      float mc = -INFINITY;
+#pragma unroll
+      for (int tt = 0; tt < 2; tt++)
+#pragma unroll
+        for (int r = 0; r < 4; r++) {
+          u[tt][r] = vp[tt][r] >= 0 ? sc[tt][r] * c_log2 : -INFINITY;
+          mc = fmaxf(mc, u[tt][r]);
+        }
+      const float mn = fmaxf(m, xgroup_max(mc));
+      const float alpha = rescale(m, mn);
+      float pr[2][4];
+      float ps = 0.f;
+#pragma unroll
+      for (int tt = 0; tt < 2; tt++)
+#pragma unroll
+        for (int r = 0; r < 4; r++) {
+          pr[tt][r] = u[tt][r] == -INFINITY ? 0.f : exp2f(u[tt][r] - mn);
+          ps += pr[tt][r];
+        }
+      l = l * alpha + ps;
+      m = mn;
+      if (__builtin_amdgcn_read_exec() & __ballot(alpha != 1.f)) {
+#pragma unroll
+        for (int j = 0; j < 8; j++) o[j] *= alpha;
+      }
+      uint4 pb = make_uint4(pack_bf16(pr[0][0], pr[0][1]), pack_bf16(pr[0][2], pr[0][3]),
+                            pack_bf16(pr[1][0], pr[1][1]), pack_bf16(pr[1][2], pr[1][3]));
+      const bf16x8 pf = __builtin_bit_cast(bf16x8, pb);
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+      for (int j = 0; j < 8; j++) {
+        const uint2 lo = *reinterpret_cast<const uint2*>(vt + (rbase ^ (vt_addr(16 * j, 0) ^ vt_addr(0, 0))));
+        const uint2 hi = *reinterpret_cast<const uint2*>(vt + (rbase ^ (vt_addr(16 * j, 4) ^ vt_addr(0, 0))));
+        const bf16x8 af = __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+        o[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, pf, o[j], 0, 0, 0);
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
+  }
+  l = xgroup_sum(l);
+  if (col >= G) return;
+  const size_t head = (size_t)bt * Hq + g * G + col;
+  if (S == 1) {
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    uint16_t* orow = static_cast<uint16_t*>(out) + head * kD + 4 * grp;
+#pragma unroll
+    for (int j = 0; j < 8; j++) {
+      const uint2 w = make_uint2(pack_bf16(o[j][0] * inv, o[j][1] * inv), pack_bf16(o[j][2] * inv, o[j][3] * inv));
+      *reinterpret_cast<uint2*>(orow + 16 * j) = w;
+    }
+    if (grp == 0 && lse) lse[head] = l > 0.f ? (m + log2f(l)) * kLn2 : -INFINITY;
+  } else {
+    float* rec = partials + (head * S + split) * kPart;
+#pragma unroll
+    for (int j = 0; j < 8; j++)
+      *reinterpret_cast<float4*>(rec + 4 + 16 * j + 4 * grp) = make_float4(o[j][0], o[j][1], o[j][2], o[j][3]);
+    if (grp == 0) {
+      rec[0] = m;
+      rec[1] = l;
+    }
+  }
+}
+
 // Merges the S split states of each (query, head), S <= kMaxSplits.
 // grid (B*T*Hq), block D. The split weights exp2(m_s - M) go to LDS first so
 // the S loads of each output element are independent of one another.
@@ -360,10 +576,16 @@ int launch_index_path(const void* q, const void* kc, const void* vc, const int32
                       float c_log2, const AttnSplit& sp, float* partials, hipStream_t stream) {
   const int nw = waves_for(Hkv);
   dim3 grid(sp.splits, B * T, Hkv / nw);
-  hipLaunchKernelGGL((attn_split_kernel<DT, G>), grid, dim3(kWave * nw), 0, stream,
-                     static_cast<const char*>(q), static_cast<const char*>(kc),
-                     static_cast<const char*>(vc), idx, k, out, lse, T, Hkv, kv_len, L_cap, c_log2,
-                     sp.rows_per_split, partials);
+  if (DT == CLSA_BF16)
+    hipLaunchKernelGGL((attn_split_mfma<G>), grid, dim3(kWave * nw), 0, stream,
+                       static_cast<const char*>(q), static_cast<const char*>(kc),
+                       static_cast<const char*>(vc), idx, k, out, lse, T, Hkv, kv_len, L_cap,
+                       c_log2, sp.rows_per_split, partials);
+  else
+    hipLaunchKernelGGL((attn_split_kernel<DT, G>), grid, dim3(kWave * nw), 0, stream,
+                       static_cast<const char*>(q), static_cast<const char*>(kc),
+                       static_cast<const char*>(vc), idx, k, out, lse, T, Hkv, kv_len, L_cap,
+                       c_log2, sp.rows_per_split, partials);
   int rc = check_launch("attn_split");
   if (rc || sp.splits == 1) return rc;
   hipLaunchKernelGGL((attn_combine_kernel<DT>), dim3(B * T * Hkv * G), dim3(kD), 0, stream,
