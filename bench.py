@@ -189,9 +189,12 @@ def main():
         graph_ms = (time.perf_counter() - t2) * 1e3 / K
         print(f"[bench] graph replay: {graph_ms * 1e3:.1f} us/step", file=sys.stderr, flush=True)
 
-    # Per-kernel averages: R back-to-back launches of one entry point on the
-    # stream, bracketed by one event pair (no event between launches, which
-    # would serialise the queue), same shapes and inputs as the step.
+    # Per-kernel averages: R back-to-back calls of one entry point, same
+    # shapes and inputs as the step. The R calls are captured once in a HIP
+    # graph and replayed between one event pair on the replay stream, so the
+    # figure is GPU time per call (the gap between a call's kernels
+    # included) without the Python call overhead; --no-graph times the
+    # direct calls instead (host-bound for short kernels).
     f0 = wl.f_layers[0]
     R = max(4 * K, 64)
     scores = torch.empty((wl.B, wl.T, wl.kv_len), dtype=torch.float32, device="cuda")
@@ -204,13 +207,32 @@ def main():
     lse = [torch.empty((wl.B, wl.T, wl.Hq), dtype=torch.float32, device="cuda") for _ in range(n)]
 
     def per_launch_us(fn):
-        for i in range(3):
-            fn(i)
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        if args.no_graph:
+            for i in range(3):
+                fn(i)
+            torch.cuda.synchronize()
+            a.record()
+            for i in range(R):
+                fn(i)
+            b.record()
+            torch.cuda.synchronize()
+            return a.elapsed_time(b) * 1e3 / R
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for i in range(3):
+                fn(i)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(R):
+                fn(i)
+        g.replay()
         torch.cuda.synchronize()
         a.record()
-        for i in range(R):
-            fn(i)
+        g.replay()
         b.record()
         torch.cuda.synchronize()
         return a.elapsed_time(b) * 1e3 / R
@@ -278,7 +300,7 @@ def main():
         "achieved_hbm_gbs_step": step_bytes / (ms_per_step * 1e-3) / 1e9,
         "roofline": {
             "bound": "hbm",
-            "kernel": "sparse_attn (attn_split_kernel + attn_combine_kernel per call)",
+            "kernel": "sparse_attn call (attn_split_mfma + attn_combine_kernel)",
             "achieved": attn_gbs,
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
