@@ -347,6 +347,123 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
+// One 32-entry step of a wave: gathered K (MFMA A layout) and V (row
+// pieces) fragments and the positions that mask them.
+struct KvStep {
+  bf16x8 kf[2][4];
+  uint4 vf[2][4];
+  uint32_t valid;  // bit 4 * tile + r: key 16 * tile + 4 * grp + r is visible
+};
+
+// Issues the loads of the step at entries [base, base + 32) of the LDS tile
+// (entries past the tile's count hold -1, so the reads need no guard).
+__device__ __forceinline__ void kv_issue(KvStep& f, const int* s_pos, int base, int col, int grp,
+                                         const char* kb, const char* vb, size_t tok) {
+  int kp[2];
+  int4 vq[2];
+#pragma unroll
+  for (int tt = 0; tt < 2; tt++) {
+    kp[tt] = s_pos[base + 16 * tt + col];
+    vq[tt] = *reinterpret_cast<const int4*>(s_pos + base + 16 * tt + 4 * grp);
+  }
+  const int vp[2][4] = {{vq[0].x, vq[0].y, vq[0].z, vq[0].w}, {vq[1].x, vq[1].y, vq[1].z, vq[1].w}};
+  f.valid = 0u;
+#pragma unroll
+  for (int tt = 0; tt < 2; tt++)
+#pragma unroll
+    for (int r = 0; r < 4; r++) f.valid |= (vp[tt][r] >= 0 ? 1u : 0u) << (4 * tt + r);
+#pragma unroll
+  for (int tt = 0; tt < 2; tt++)
+#pragma unroll
+    for (int ks = 0; ks < 4; ks++)
+      f.kf[tt][ks] = __builtin_bit_cast(
+          bf16x8, *reinterpret_cast<const uint4*>(kb + (size_t)max(kp[tt], 0) * tok + 64 * ks));
+#pragma unroll
+  for (int tt = 0; tt < 2; tt++)
+#pragma unroll
+    for (int r = 0; r < 4; r++)
+      f.vf[tt][r] = *reinterpret_cast<const uint4*>(vb + (size_t)max(vp[tt][r], 0) * tok);
+}
+
+// Running state of one wave: O^T accumulators, max and sum of head col.
+struct MfmaState {
+  f32x4 o[8];
+  float m, l;
+};
+
+__device__ __forceinline__ void kv_consume(const KvStep& f, MfmaState& st, const bf16x8 (&qf)[4],
+                                           char* vt, int wbase, int rbase, float c_log2) {
+  f32x4 sc[2];
+#pragma unroll
+  for (int tt = 0; tt < 2; tt++) {
+    sc[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < 4; ks++) sc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.kf[tt][ks], qf[ks], sc[tt], 0, 0, 0);
+  }
+  // Stage V^T while the scores are in flight.
+#pragma unroll
+  for (int tt = 0; tt < 2; tt++) {
+    const uint32_t* w0 = reinterpret_cast<const uint32_t*>(&f.vf[tt][0]);
+    const uint32_t* w1 = reinterpret_cast<const uint32_t*>(&f.vf[tt][1]);
+    const uint32_t* w2 = reinterpret_cast<const uint32_t*>(&f.vf[tt][2]);
+    const uint32_t* w3 = reinterpret_cast<const uint32_t*>(&f.vf[tt][3]);
+#pragma unroll
+    for (int e = 0; e < 8; e++) {
+      const int off = wbase ^ (vt_addr(e, 4 * tt) ^ vt_addr(0, 0));
+      *reinterpret_cast<uint2*>(vt + off) = pack4(w0[e / 2], w1[e / 2], w2[e / 2], w3[e / 2], e & 1);
+    }
+  }
+  // Online softmax of head col over the 32 keys.
+  float u[2][4];
+  float mc = -INFINITY;
+#pragma unroll
+  for (int tt = 0; tt < 2; tt++)
+#pragma unroll
+    for (int r = 0; r < 4; r++) {
+      u[tt][r] = (f.valid >> (4 * tt + r) & 1u) ? sc[tt][r] * c_log2 : -INFINITY;
+      mc = fmaxf(mc, u[tt][r]);
+    }
+  const float mn = fmaxf(st.m, xgroup_max(mc));
+  const float alpha = rescale(st.m, mn);
+  float pr[2][4];
+  float ps = 0.f;
+#pragma unroll
+  for (int tt = 0; tt < 2; tt++)
+#pragma unroll
+    for (int r = 0; r < 4; r++) {
+      pr[tt][r] = u[tt][r] == -INFINITY ? 0.f : exp2f(u[tt][r] - mn);
+      ps += pr[tt][r];
+    }
+  st.l = st.l * alpha + ps;
+  st.m = mn;
+  if (__builtin_amdgcn_read_exec() & __ballot(alpha != 1.f)) {
+#pragma unroll
+    for (int j = 0; j < 8; j++) st.o[j] *= alpha;
+  }
+  const uint4 pb = make_uint4(pack_bf16(pr[0][0], pr[0][1]), pack_bf16(pr[0][2], pr[0][3]),
+                              pack_bf16(pr[1][0], pr[1][1]), pack_bf16(pr[1][2], pr[1][3]));
+  const bf16x8 pf = __builtin_bit_cast(bf16x8, pb);
+  // The tile is private to the wave; the fences keep the compiler from
+  // moving its accesses across the write/read phases.
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  uint2 lo[8], hi[8];
+#pragma unroll
+  for (int j = 0; j < 8; j++) {
+    lo[j] = *reinterpret_cast<const uint2*>(vt + (rbase ^ (vt_addr(16 * j, 0) ^ vt_addr(0, 0))));
+    hi[j] = *reinterpret_cast<const uint2*>(vt + (rbase ^ (vt_addr(16 * j, 4) ^ vt_addr(0, 0))));
+  }
+#pragma unroll
+  for (int j = 0; j < 8; j++) {
+    const bf16x8 af = __builtin_bit_cast(bf16x8, make_uint4(lo[j].x, lo[j].y, hi[j].x, hi[j].y));
+    st.o[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, pf, st.o[j], 0, 0, 0);
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 template <int G>
 __global__ __launch_bounds__(kWave * kMaxWaves) void attn_split_mfma(
     const char* __restrict__ q, const char* __restrict__ kc, const char* __restrict__ vc,
@@ -354,7 +471,7 @@ __global__ __launch_bounds__(kWave * kMaxWaves) void attn_split_mfma(
     int T, int Hkv, int kv_len, int L_cap, float c_log2, int rows_per_split,
     float* __restrict__ partials) {
   constexpr int ROW = kD * 2;
-  __shared__ int s_pos[kTileRows];
+  __shared__ __attribute__((aligned(16))) int s_pos[kTileRows];
   __shared__ __attribute__((aligned(16))) char s_vt[kMaxWaves * kVtBytes];
   const int lane = threadIdx.x % kWave;
   const int wave = threadIdx.x / kWave;
@@ -380,10 +497,11 @@ __global__ __launch_bounds__(kWave * kMaxWaves) void attn_split_mfma(
       u = *reinterpret_cast<const uint4*>(q + (((size_t)bt * Hq + g * G + col) * kD + 8 * grp + 32 * ks) * 2);
     qf[ks] = __builtin_bit_cast(bf16x8, u);
   }
-  f32x4 o[8];
+  MfmaState st;
 #pragma unroll
-  for (int j = 0; j < 8; j++) o[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m = -INFINITY, l = 0.f;  // head col; m shared by the lane groups, l per group
+  for (int j = 0; j < 8; j++) st.o[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  st.m = -INFINITY;  // head col; shared by the four lane groups
+  st.l = 0.f;        // this lane group's keys only
 
   // LDS offsets: the write addresses depend on the lane and on (e, tile)
   // only through XOR with a constant, likewise the reads on (j, tile).
@@ -396,104 +514,23 @@ __global__ __launch_bounds__(kWave * kMaxWaves) void attn_split_mfma(
 
   for (int t0 = r0; t0 < r1; t0 += kTileRows) {  // uniform over the workgroup
     const int n = min(kTileRows, r1 - t0);
+    const int n_pad = (n + 31) / 32 * 32;  // every entry a step can read
     __syncthreads();
-    for (int i = threadIdx.x; i < n; i += blockDim.x) {
-      const int p = irow[t0 + i];
+    for (int i = threadIdx.x; i < n_pad; i += blockDim.x) {
+      const int p = i < n ? irow[t0 + i] : -1;
       s_pos[i] = (p >= 0 && p < vis) ? p : -1;
     }
     __syncthreads();
+    // One 32-entry step at a time: at the usual split sizes a wave has one
+    // or two steps, and the other waves of the SIMD cover its load latency.
     for (int base = 0; base < n; base += 32) {  // uniform over the wave
-      int kp[2], vp[2][4];
-#pragma unroll
-      for (int tt = 0; tt < 2; tt++) {
-        const int rk = base + 16 * tt + col;
-        kp[tt] = rk < n ? s_pos[rk] : -1;
-#pragma unroll
-        for (int r = 0; r < 4; r++) {
-          const int rv = base + 16 * tt + 4 * grp + r;
-          vp[tt][r] = rv < n ? s_pos[rv] : -1;
-        }
-      }
-      bf16x8 kf[2][4];
-      uint4 vf[2][4];
-#pragma unroll
-      for (int tt = 0; tt < 2; tt++)
-#pragma unroll
-        for (int ks = 0; ks < 4; ks++)
-          kf[tt][ks] = __builtin_bit_cast(
-              bf16x8, *reinterpret_cast<const uint4*>(kb + (size_t)max(kp[tt], 0) * tok + 64 * ks));
-#pragma unroll
-      for (int tt = 0; tt < 2; tt++)
-#pragma unroll
-        for (int r = 0; r < 4; r++)
-          vf[tt][r] = *reinterpret_cast<const uint4*>(vb + (size_t)max(vp[tt][r], 0) * tok);
-      f32x4 sc[2];
-#pragma unroll
-      for (int tt = 0; tt < 2; tt++) {
-        sc[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < 4; ks++) sc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[tt][ks], qf[ks], sc[tt], 0, 0, 0);
-      }
-      // Stage V^T while the scores are in flight.
-#pragma unroll
-      for (int tt = 0; tt < 2; tt++) {
-        const uint32_t* w0 = reinterpret_cast<const uint32_t*>(&vf[tt][0]);
-        const uint32_t* w1 = reinterpret_cast<const uint32_t*>(&vf[tt][1]);
-        const uint32_t* w2 = reinterpret_cast<const uint32_t*>(&vf[tt][2]);
-        const uint32_t* w3 = reinterpret_cast<const uint32_t*>(&vf[tt][3]);
-#pragma unroll
-        for (int e = 0; e < 8; e++) {
-          const int off = wbase ^ (vt_addr(e, 4 * tt) ^ vt_addr(0, 0));
-          *reinterpret_cast<uint2*>(vt + off) =
-              pack4(w0[e / 2], w1[e / 2], w2[e / 2], w3[e / 2], e & 1);
-        }
-      }
-      // Online softmax of head col over the 32 keys.
-      float u[2][4];
-      float mc = -INFINITY;
-#pragma unroll
-      for (int tt = 0; tt < 2; tt++)
-#pragma unroll
-        for (int r = 0; r < 4; r++) {
-          u[tt][r] = vp[tt][r] >= 0 ? sc[tt][r] * c_log2 : -INFINITY;
-          mc = fmaxf(mc, u[tt][r]);
-        }
-      const float mn = fmaxf(m, xgroup_max(mc));
-      const float alpha = rescale(m, mn);
-      float pr[2][4];
-      float ps = 0.f;
-#pragma unroll
-      for (int tt = 0; tt < 2; tt++)
-#pragma unroll
-        for (int r = 0; r < 4; r++) {
-          pr[tt][r] = u[tt][r] == -INFINITY ? 0.f : exp2f(u[tt][r] - mn);
-          ps += pr[tt][r];
-        }
-      l = l * alpha + ps;
-      m = mn;
-      if (__builtin_amdgcn_read_exec() & __ballot(alpha != 1.f)) {
-#pragma unroll
-        for (int j = 0; j < 8; j++) o[j] *= alpha;
-      }
-      uint4 pb = make_uint4(pack_bf16(pr[0][0], pr[0][1]), pack_bf16(pr[0][2], pr[0][3]),
-                            pack_bf16(pr[1][0], pr[1][1]), pack_bf16(pr[1][2], pr[1][3]));
-      const bf16x8 pf = __builtin_bit_cast(bf16x8, pb);
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-#pragma unroll
-      for (int j = 0; j < 8; j++) {
-        const uint2 lo = *reinterpret_cast<const uint2*>(vt + (rbase ^ (vt_addr(16 * j, 0) ^ vt_addr(0, 0))));
-        const uint2 hi = *reinterpret_cast<const uint2*>(vt + (rbase ^ (vt_addr(16 * j, 4) ^ vt_addr(0, 0))));
-        const bf16x8 af = __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
-        o[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, pf, o[j], 0, 0, 0);
-      }
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      KvStep f;
+      kv_issue(f, s_pos, base, col, grp, kb, vb, tok);
+      kv_consume(f, st, qf, vt, wbase, rbase, c_log2);
     }
   }
-  l = xgroup_sum(l);
+  const float l = xgroup_sum(st.l);
+  const float m = st.m;
   if (col >= G) return;
   const size_t head = (size_t)bt * Hq + g * G + col;
   if (S == 1) {
@@ -501,7 +538,8 @@ __global__ __launch_bounds__(kWave * kMaxWaves) void attn_split_mfma(
     uint16_t* orow = static_cast<uint16_t*>(out) + head * kD + 4 * grp;
 #pragma unroll
     for (int j = 0; j < 8; j++) {
-      const uint2 w = make_uint2(pack_bf16(o[j][0] * inv, o[j][1] * inv), pack_bf16(o[j][2] * inv, o[j][3] * inv));
+      const uint2 w = make_uint2(pack_bf16(st.o[j][0] * inv, st.o[j][1] * inv),
+                                 pack_bf16(st.o[j][2] * inv, st.o[j][3] * inv));
       *reinterpret_cast<uint2*>(orow + 16 * j) = w;
     }
     if (grp == 0 && lse) lse[head] = l > 0.f ? (m + log2f(l)) * kLn2 : -INFINITY;
@@ -509,7 +547,8 @@ __global__ __launch_bounds__(kWave * kMaxWaves) void attn_split_mfma(
     float* rec = partials + (head * S + split) * kPart;
 #pragma unroll
     for (int j = 0; j < 8; j++)
-      *reinterpret_cast<float4*>(rec + 4 + 16 * j + 4 * grp) = make_float4(o[j][0], o[j][1], o[j][2], o[j][3]);
+      *reinterpret_cast<float4*>(rec + 4 + 16 * j + 4 * grp) =
+          make_float4(st.o[j][0], st.o[j][1], st.o[j][2], st.o[j][3]);
     if (grp == 0) {
       rec[0] = m;
       rec[1] = l;
