@@ -107,6 +107,7 @@ TOPK_CASES = [
     ("strided", 1, 1, 131072, 3000),   # a strided sample sees only the high positions: full-row redo
     ("strided", 2, 1, 131072, 1000),
     ("needle", 2, 1, 131073, 2048),    # misaligned second row
+    ("desc", 1, 1, 40000, 2048),       # the top k fill one 4096-chunk: its candidate segment overflows
 ]
 
 

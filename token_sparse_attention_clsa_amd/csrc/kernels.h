@@ -14,10 +14,12 @@ int launch_index_score(const void* q_idx, const void* k_idx, int idx_dtype, cons
 bool index_score_supported(int idx_dtype, int H_I, int D_I);
 
 // ---- top-k -----------------------------------------------------------------
-// Buffers: counts [rows * nchunks] u32, cand [rows * nchunks * kTopkChunk] i32,
-// spill [rows * kv_len] i32 (used only when a row is redone in full).
+// Buffers: counts [rows * nchunks] u32, cand [rows * nchunks * kTopkSegCap]
+// (position, key) pairs of i32, spill [rows * kv_len] i32 (used only when a
+// row is redone in full).
 constexpr int kTopkBins = 4096;
 constexpr int kTopkChunk = 4096;
+constexpr int kTopkSegCap = 1024;     // candidates kept per chunk
 constexpr int kTopkMaxChunks = 1024;  // kv_len <= 4M
 struct TopkBuffers {
   int nchunks;

@@ -12,18 +12,19 @@
 //      takes the same deterministic strided sample of the row, histograms the
 //      sample's top digits in LDS and picks the bin where the sample's count
 //      from the top reaches about twice the rank k would have in the sample.
-//      It then writes, in position order, the positions of its 4096-element
-//      chunk whose top digit is at or above that bin, and their count. With a
-//      2048-element sample the chance that this keeps fewer than k positions
-//      is negligible for any smooth score distribution, and the next kernel
-//      checks it anyway.
+//      It then writes, in position order, the (position, key) pairs of its
+//      4096-element chunk whose top digit is at or above that bin (at most
+//      kTopkSegCap of them) and their count. With a 2048-element sample the
+//      chance that this keeps fewer than k positions, or more than the cap in
+//      a chunk, is negligible for any smooth score distribution, and the next
+//      kernel checks both anyway.
 //   2. topk_select (rows, 1024 threads): gathers the candidate segments (in
 //      chunk order, hence position order) into LDS and resolves the k-th key
 //      theta exactly with three LDS histograms, then emits, in one ordered
 //      scan, keys above theta and the first `quota` keys equal to theta. If
-//      the candidates number fewer than k, it redoes the row on its own (LDS
-//      histogram of the full row, ordered candidate pass), so the result is
-//      exact whatever the sample did.
+//      the candidates number fewer than k or a chunk overflowed its segment,
+//      it redoes the row on its own (LDS histogram of the full row, ordered
+//      candidate pass), so the result is exact whatever the sample did.
 // Rows whose visible count is <= k take every visible position.
 #include "kernels.h"
 
@@ -86,19 +87,19 @@ struct Cand {
 // Candidates still in the filter's chunk segments: candidate i lives in the
 // chunk c with off[c] <= i < off[c + 1].
 struct SegCand {
-  const int32_t* seg;  // the row's segments, kChunk entries each
-  const int* off;      // LDS, nchunks + 1 exclusive offsets
+  const int2* seg;  // the row's segments, kTopkSegCap (position, key) pairs each
+  const int* off;   // LDS, nchunks + 1 exclusive offsets
   int nchunks;
-  const float* srow;
-  __device__ int p(int i) const {
+  __device__ int2 e(int i) const {
     int lo = 0, hi = nchunks;
     while (hi - lo > 1) {
       const int mid = (lo + hi) / 2;
       if (off[mid] <= i) lo = mid; else hi = mid;
     }
-    return seg[(size_t)lo * kChunk + (i - off[lo])];
+    return seg[(size_t)lo * kTopkSegCap + (i - off[lo])];
   }
-  __device__ uint32_t k(int i) const { return score_key(srow[p(i)]); }
+  __device__ int p(int i) const { return e(i).x; }
+  __device__ uint32_t k(int i) const { return (uint32_t)e(i).y; }
 };
 
 // Resolves theta among the candidates and emits the row's selection.
@@ -290,7 +291,7 @@ __device__ int histogram_and_candidates(const float* srow, int vis, int k, uint3
 // grid (nchunks, rows), block 256.
 __global__ __launch_bounds__(kFilterThreads) void topk_filter(const float* __restrict__ scores,
                                                               uint32_t* __restrict__ counts,
-                                                              int32_t* __restrict__ cand, int T,
+                                                              int2* __restrict__ cand, int T,
                                                               int kv_len, int k, int nchunks) {
   __shared__ uint32_t h[kBins0];
   __shared__ int tmp[17];
@@ -319,37 +320,45 @@ __global__ __launch_bounds__(kFilterThreads) void topk_filter(const float* __res
   const int e0 = c0 + threadIdx.x * 16;
   uint32_t flags = 0;
   int c = 0;
+  uint32_t key[16];
   if (e0 + 15 < vis && (reinterpret_cast<uintptr_t>(srow + e0) & 15) == 0) {
     const float4* p4 = reinterpret_cast<const float4*>(srow + e0);
     float4 v[4] = {p4[0], p4[1], p4[2], p4[3]};
     const float* x = reinterpret_cast<const float*>(v);
 #pragma unroll
-    for (int j = 0; j < 16; j++)
-      if ((score_key(x[j]) >> 20) >= b0) {
+    for (int j = 0; j < 16; j++) {
+      key[j] = score_key(x[j]);
+      if ((key[j] >> 20) >= b0) {
         flags |= 1u << j;
         c++;
       }
+    }
   } else {
 #pragma unroll
-    for (int j = 0; j < 16; j++)
-      if (e0 + j < vis && (score_key(srow[e0 + j]) >> 20) >= b0) {
+    for (int j = 0; j < 16; j++) {
+      key[j] = e0 + j < vis ? score_key(srow[e0 + j]) : 0u;
+      if (e0 + j < vis && (key[j] >> 20) >= b0) {
         flags |= 1u << j;
         c++;
       }
+    }
   }
   int total;
   int o = block_exclusive_scan(c, tmp, &total);
-  int32_t* seg = cand + ((size_t)row * nchunks + blockIdx.x) * kChunk;
+  int2* seg = cand + ((size_t)row * nchunks + blockIdx.x) * kTopkSegCap;
 #pragma unroll
   for (int j = 0; j < 16; j++)
-    if (flags >> j & 1u) seg[o++] = e0 + j;
-  if (threadIdx.x == 0) *cnt = (uint32_t)total;
+    if (flags >> j & 1u) {
+      if (o < kTopkSegCap) seg[o] = make_int2(e0 + j, (int)key[j]);
+      o++;
+    }
+  if (threadIdx.x == 0) *cnt = (uint32_t)total;  // above kTopkSegCap: the row is redone
 }
 
 // grid (rows), block 1024.
 __global__ __launch_bounds__(kThreads) void topk_select(const float* __restrict__ scores,
                                                         const uint32_t* __restrict__ counts,
-                                                        const int32_t* __restrict__ cand,
+                                                        const int2* __restrict__ cand,
                                                         int32_t* __restrict__ spill,
                                                         int32_t* __restrict__ idx, int T,
                                                         int kv_len, int k, int nchunks) {
@@ -370,30 +379,38 @@ __global__ __launch_bounds__(kThreads) void topk_select(const float* __restrict_
   const float* srow = scores + (size_t)row * kv_len;
   // Offsets of the candidate segments (nchunks <= kThreads).
   int n;
+  bool overflow;
   {
     const int c = threadIdx.x;
     const int v = c < nchunks ? (int)counts[(size_t)row * nchunks + c] : 0;
     const int o = block_exclusive_scan(v, tmp, &n);
     if (c < nchunks) off[c] = o;
     if (c == 0) off[nchunks] = n;
+    overflow = __syncthreads_or(v > kTopkSegCap) != 0;
   }
-  __syncthreads();
-  if (n >= k) {
-    SegCand seg{cand + (size_t)row * nchunks * kChunk, off, nchunks, srow};
+  if (n >= k && !overflow) {
+    const int2* segs = cand + (size_t)row * nchunks * kTopkSegCap;
     if (n <= kLdsCap) {
-      for (int i = threadIdx.x; i < n; i += kThreads) {
-        const int p = seg.p(i);
-        lpos[i] = p;
-        lkey[i] = score_key(srow[p]);
+      // tpc threads per chunk copy its segment to the LDS slots off[c]...
+      const int tpc = nchunks >= kThreads ? 1 : kThreads / nchunks;
+      for (int c = threadIdx.x / tpc; c < nchunks; c += kThreads / tpc) {
+        const int2* sg = segs + (size_t)c * kTopkSegCap;
+        const int o = off[c], cnt = off[c + 1] - off[c];
+        for (int j = threadIdx.x % tpc; j < cnt; j += tpc) {
+          const int2 e = sg[j];
+          lpos[o + j] = e.x;
+          lkey[o + j] = (uint32_t)e.y;
+        }
       }
       __syncthreads();
       select_top(Cand{lpos, lkey, nullptr, srow}, n, k, h, res, tmp, out);
     } else {
-      select_top(seg, n, k, h, res, tmp, out);
+      select_top(SegCand{segs, off, nchunks}, n, k, h, res, tmp, out);
     }
     return;
   }
-  // The sample overshot: redo this row from its scores alone.
+  // The sample overshot (or a chunk overflowed): redo this row from its
+  // scores alone.
   int32_t* gpos = spill + (size_t)row * kv_len;
   uint32_t b0;
   int above;
@@ -418,7 +435,7 @@ TopkBuffers topk_buffers(int rows, int kv_len) {
   TopkBuffers b;
   b.nchunks = (kv_len + kChunk - 1) / kChunk;
   b.counts_words = (size_t)rows * b.nchunks;
-  b.cand_words = (size_t)rows * b.nchunks * kChunk;
+  b.cand_words = (size_t)rows * b.nchunks * kTopkSegCap * 2;
   b.spill_words = (size_t)rows * kv_len;
   return b;
 }
@@ -429,11 +446,12 @@ int launch_topk(const float* scores, int B, int T, int kv_len, int k, int32_t* i
   const TopkBuffers tb = topk_buffers(rows, kv_len);
   if (tb.nchunks > kTopkMaxChunks)
     return set_error(CLSA_ERR_UNSUPPORTED, "topk: kv_len=%d above %d", kv_len, kTopkMaxChunks * kChunk);
+  int2* segs = reinterpret_cast<int2*>(cand);
   hipLaunchKernelGGL(topk_filter, dim3(tb.nchunks, rows), dim3(kFilterThreads), 0, stream, scores,
-                     counts, cand, T, kv_len, k, tb.nchunks);
+                     counts, segs, T, kv_len, k, tb.nchunks);
   int rc = check_launch("topk_filter");
   if (rc) return rc;
-  hipLaunchKernelGGL(topk_select, dim3(rows), dim3(kThreads), 0, stream, scores, counts, cand, spill,
+  hipLaunchKernelGGL(topk_select, dim3(rows), dim3(kThreads), 0, stream, scores, counts, segs, spill,
                      idx, T, kv_len, k, tb.nchunks);
   return check_launch("topk_select");
 }
