@@ -104,8 +104,9 @@ size_t clsa_workspace_bytes(int op, int B, int T, int Hq, int Hkv, int D,
  *   w      [B, T, H_I]       float32 head weights
  *   scores [B, T, kv_len]    float32 output
  * Accumulation is float32. BF16 and FP8 run on matrix cores and need
- * H_I in {16, 32, 48, 64} and D_I in {64, 128}; F32 takes any H_I <= 64,
- * D_I <= 256. Pointers must be 16-byte aligned.
+ * H_I in {16, 32, 48, 64} and D_I in {64, 128}; F32 takes any H_I, D_I
+ * with H_I * D_I <= 8192. Other shapes return CLSA_ERR_UNSUPPORTED.
+ * Pointers must be 16-byte aligned.
  */
 int clsa_index_score(const void* q_idx, const void* k_idx, int idx_dtype,
                      const float* w, float* scores, int B, int T, int H_I,
@@ -145,7 +146,9 @@ int clsa_topk(const float* scores, int B, int T, int kv_len, int k,
  *   idx     [B, T, k]             int32
  *   out     [B, T, Hq, D]         dtype output (BF16 rounded once, to nearest even)
  *   lse     [B, T, Hq]            float32 output, or NULL
- * scale <= 0 selects 1/sqrt(D). Softmax and accumulation are float32.
+ * scale <= 0 selects 1/sqrt(D). Softmax and accumulation are float32; with
+ * BF16 the probabilities enter the matrix-core P.V product rounded to bf16
+ * (the normaliser stays float32), F32 keeps them in float32.
  * Supported: D = 128, Hq / Hkv in {1, 2, 4, 8}.
  * Workspace: clsa_workspace_bytes(CLSA_OP_SPARSE_ATTN, B, T, Hq, Hkv, D, 0, k, 0).
  */
