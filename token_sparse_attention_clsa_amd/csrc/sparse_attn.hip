@@ -8,16 +8,17 @@
 // reuses the one index).
 //
 // Work split (index path): one workgroup per (query, split of the k
-// entries, block of KV heads), one wave per KV head. The split's index
-// entries are staged once in LDS and shared by the waves, so the waves of a
+// entries, block of KV heads), one wave per KV head, so the waves of a
 // workgroup read the same tokens' K/V rows (contiguous across KV heads in the
-// token-major cache) at about the same time. A row of one KV head is D
-// contiguous elements, gathered by 16 lanes with one 16-byte load each
-// (bf16), four rows per wave instruction; each lane group keeps 8 rows of K
-// and V in flight before computing. Scores use v_dot2_f32_bf16 on bf16 pairs
-// and a 16-lane DPP butterfly; softmax runs online in the log2 domain in
-// float32 with one rescale per 8-row step; the G query heads of a KV head
-// share every gathered row, so each row leaves HBM once per layer.
+// token-major cache) at about the same time, and each row leaves HBM once per
+// layer for all G query heads of its KV head.
+//  - bf16 (attn_split_mfma): q.K and P.V on matrix cores, 32 entries per
+//    step; described above the kernel.
+//  - fp32 (attn_split_kernel): the split's entries are staged in LDS; a row
+//    of one KV head is gathered by 16 lanes with one 16-byte load each, four
+//    rows per wave instruction; scores are fp32 dot products with a 16-lane
+//    DPP butterfly; softmax runs online in the log2 domain with one rescale
+//    per 8-row step.
 // With several splits, each split writes its (max, sum, unnormalised
 // output) state and a second small kernel merges the states of a head in
 // split order (deterministic). Merging inside the first kernel would need an
@@ -41,44 +42,9 @@ typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
 template <int DT>
 struct AttnElem;
 template <>
-struct AttnElem<CLSA_BF16> {
-  static constexpr int bytes = 2;
-  static constexpr int rows_per_step = 8;  // rows per lane group kept in flight
-  struct Frag {
-    uint4 u;  // 8 bf16
-  };
-  static __device__ __forceinline__ Frag load(const char* p) {
-    return Frag{*reinterpret_cast<const uint4*>(p)};
-  }
-  static __device__ __forceinline__ float dot(const Frag& q, const Frag& k) {
-    float s = 0.f;
-    s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, q.u.x),
-                                        __builtin_bit_cast(bf16x2, k.u.x), s, false);
-    s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, q.u.y),
-                                        __builtin_bit_cast(bf16x2, k.u.y), s, false);
-    s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, q.u.z),
-                                        __builtin_bit_cast(bf16x2, k.u.z), s, false);
-    s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, q.u.w),
-                                        __builtin_bit_cast(bf16x2, k.u.w), s, false);
-    return s;
-  }
-  static __device__ __forceinline__ void to_f32(const Frag& v, float* f) {
-    f[0] = bf16_lo(v.u.x); f[1] = bf16_hi(v.u.x);
-    f[2] = bf16_lo(v.u.y); f[3] = bf16_hi(v.u.y);
-    f[4] = bf16_lo(v.u.z); f[5] = bf16_hi(v.u.z);
-    f[6] = bf16_lo(v.u.w); f[7] = bf16_hi(v.u.w);
-  }
+struct AttnElem<CLSA_BF16> {  // output stores of the combine kernel
   static __device__ __forceinline__ void store(void* out, size_t i, float x) {
     static_cast<uint16_t*>(out)[i] = (uint16_t)f32_to_bf16_rne(x);
-  }
-  // 8 consecutive outputs starting at element i (16-byte aligned).
-  static __device__ __forceinline__ void store8(void* out, size_t i, const float* x) {
-    uint4 u;
-    u.x = f32_to_bf16_rne(x[0]) | (f32_to_bf16_rne(x[1]) << 16);
-    u.y = f32_to_bf16_rne(x[2]) | (f32_to_bf16_rne(x[3]) << 16);
-    u.z = f32_to_bf16_rne(x[4]) | (f32_to_bf16_rne(x[5]) << 16);
-    u.w = f32_to_bf16_rne(x[6]) | (f32_to_bf16_rne(x[7]) << 16);
-    *reinterpret_cast<uint4*>(static_cast<uint16_t*>(out) + i) = u;
   }
 };
 template <>
@@ -355,18 +321,25 @@ struct KvStep {
   uint32_t valid;  // bit 4 * tile + r: key 16 * tile + 4 * grp + r is visible
 };
 
-// Issues the loads of the step at entries [base, base + 32) of the LDS tile
-// (entries past the tile's count hold -1, so the reads need no guard).
-__device__ __forceinline__ void kv_issue(KvStep& f, const int* s_pos, int base, int col, int grp,
-                                         const char* kb, const char* vb, size_t tok) {
-  int kp[2];
-  int4 vq[2];
+// Issues the loads of the step at index entries [e0, e0 + 32) of the
+// query's row. Each lane reads the positions it needs straight from the
+// index row (the 32 entries share one or two cache lines); entries at or
+// past `end`, negative, or outside the visible range are masked and read
+// cache row 0.
+__device__ __forceinline__ int vis_pos(const int32_t* irow, int e, int end, int vis) {
+  const int p = e < end ? irow[e] : -1;
+  return (p >= 0 && p < vis) ? p : -1;
+}
+__device__ __forceinline__ void kv_issue(KvStep& f, const int32_t* irow, int e0, int end, int vis,
+                                         int col, int grp, const char* kb, const char* vb,
+                                         size_t tok) {
+  int kp[2], vp[2][4];
 #pragma unroll
   for (int tt = 0; tt < 2; tt++) {
-    kp[tt] = s_pos[base + 16 * tt + col];
-    vq[tt] = *reinterpret_cast<const int4*>(s_pos + base + 16 * tt + 4 * grp);
+    kp[tt] = vis_pos(irow, e0 + 16 * tt + col, end, vis);
+#pragma unroll
+    for (int r = 0; r < 4; r++) vp[tt][r] = vis_pos(irow, e0 + 16 * tt + 4 * grp + r, end, vis);
   }
-  const int vp[2][4] = {{vq[0].x, vq[0].y, vq[0].z, vq[0].w}, {vq[1].x, vq[1].y, vq[1].z, vq[1].w}};
   f.valid = 0u;
 #pragma unroll
   for (int tt = 0; tt < 2; tt++)
@@ -471,7 +444,6 @@ __global__ __launch_bounds__(kWave * kMaxWaves) void attn_split_mfma(
     int T, int Hkv, int kv_len, int L_cap, float c_log2, int rows_per_split,
     float* __restrict__ partials) {
   constexpr int ROW = kD * 2;
-  __shared__ __attribute__((aligned(16))) int s_pos[kTileRows];
   __shared__ __attribute__((aligned(16))) char s_vt[kMaxWaves * kVtBytes];
   const int lane = threadIdx.x % kWave;
   const int wave = threadIdx.x / kWave;
@@ -512,22 +484,12 @@ __global__ __launch_bounds__(kWave * kMaxWaves) void attn_split_mfma(
   const char* vb = vc + ((size_t)b * L_cap * Hkv + g) * ROW + 16 * col;
   const size_t tok = (size_t)Hkv * ROW;
 
-  for (int t0 = r0; t0 < r1; t0 += kTileRows) {  // uniform over the workgroup
-    const int n = min(kTileRows, r1 - t0);
-    const int n_pad = (n + 31) / 32 * 32;  // every entry a step can read
-    __syncthreads();
-    for (int i = threadIdx.x; i < n_pad; i += blockDim.x) {
-      const int p = i < n ? irow[t0 + i] : -1;
-      s_pos[i] = (p >= 0 && p < vis) ? p : -1;
-    }
-    __syncthreads();
-    // One 32-entry step at a time: at the usual split sizes a wave has one
-    // or two steps, and the other waves of the SIMD cover its load latency.
-    for (int base = 0; base < n; base += 32) {  // uniform over the wave
-      KvStep f;
-      kv_issue(f, s_pos, base, col, grp, kb, vb, tok);
-      kv_consume(f, st, qf, vt, wbase, rbase, c_log2);
-    }
+  // One 32-entry step at a time: at the usual split sizes a wave has one
+  // or two steps, and the other waves of the SIMD cover its load latency.
+  for (int e0 = r0; e0 < r1; e0 += 32) {  // uniform over the wave
+    KvStep f;
+    kv_issue(f, irow, e0, r1, vis, col, grp, kb, vb, tok);
+    kv_consume(f, st, qf, vt, wbase, rbase, c_log2);
   }
   const float l = xgroup_sum(st.l);
   const float m = st.m;
@@ -615,7 +577,7 @@ int launch_index_path(const void* q, const void* kc, const void* vc, const int32
                       float c_log2, const AttnSplit& sp, float* partials, hipStream_t stream) {
   const int nw = waves_for(Hkv);
   dim3 grid(sp.splits, B * T, Hkv / nw);
-  if (DT == CLSA_BF16)
+  if constexpr (DT == CLSA_BF16)
     hipLaunchKernelGGL((attn_split_mfma<G>), grid, dim3(kWave * nw), 0, stream,
                        static_cast<const char*>(q), static_cast<const char*>(kc),
                        static_cast<const char*>(vc), idx, k, out, lse, T, Hkv, kv_len, L_cap,
