@@ -34,8 +34,9 @@ int launch_topk(const float* scores, int B, int T, int kv_len, int k, int32_t* i
 // the k entries are not split).
 struct AttnSplit {
   int splits, rows_per_split;
+  int waves_per_head;  // waves sharing one split of one KV head
 };
-AttnSplit attn_split(int B, int T, int Hkv, int k);
+AttnSplit attn_split(int B, int T, int Hkv, int k, bool mfma);
 size_t attn_partial_floats(int B, int T, int Hq, int Hkv, int k);
 bool sparse_attn_supported(int dtype, int Hq, int Hkv, int D);
 int launch_sparse_attn(const void* q, const void* kc, const void* vc, int dtype, const int32_t* idx,

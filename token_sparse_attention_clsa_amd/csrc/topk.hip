@@ -129,23 +129,26 @@ __device__ void select_and_emit(const Acc& acc, int n, int need0, uint32_t b0, u
   find_bin(h, 256, need1, res, tmp);
   const uint32_t theta = (pre << 8) | (uint32_t)res[0];
   const int quota = need1 - res[1];  // how many keys equal to theta are taken
-  // Ordered emission: 4 consecutive candidates per thread per tile.
+  // Ordered emission: thread t owns the run [t0 + t * run, t0 + (t + 1) * run)
+  // of the tile (run <= 16), so up to 16 * blockDim.x candidates take one
+  // block scan and no barrier waits behind the output stores.
+  const int run = min(16, max(1, (n + (int)blockDim.x - 1) / (int)blockDim.x));
   int gt_base = 0, eq_base = 0;
-  for (int t0 = 0; t0 < n; t0 += 4 * blockDim.x) {
-    const int i0 = t0 + threadIdx.x * 4;
+  for (int t0 = 0; t0 < n; t0 += run * blockDim.x) {  // uniform over the workgroup
+    const int i0 = t0 + threadIdx.x * run;
     int gt = 0, eq = 0;
-    for (int e = 0; e < 4; e++) {
+    for (int e = 0; e < run; e++) {
       if (i0 + e < n) {
         const uint32_t key = acc.k(i0 + e);
         gt += key > theta;
         eq += key == theta;
       }
     }
-    int tot;
+    int tot;  // per tile both counts stay below 2^16
     const int pre_cnt = block_exclusive_scan((eq << 16) | gt, tmp, &tot);
     int g = gt_base + (pre_cnt & 0xffff);
     int q = eq_base + (pre_cnt >> 16);
-    for (int e = 0; e < 4; e++) {
+    for (int e = 0; e < run; e++) {
       if (i0 + e < n) {
         const uint32_t key = acc.k(i0 + e);
         if (key > theta) {
@@ -377,7 +380,22 @@ __global__ __launch_bounds__(kThreads) void topk_select(const float* __restrict_
     return;
   }
   const float* srow = scores + (size_t)row * kv_len;
-  // Offsets of the candidate segments (nchunks <= kThreads).
+  // Chunk owned by this thread for the gather: tpc threads per chunk, thread
+  // j0 of a chunk takes entries j0, j0 + tpc, ... Its first kSpec entries are
+  // loaded now, before the counts are known (the slots exist whatever the
+  // count), so the usual gather costs one memory round trip.
+  const int2* segs = cand + (size_t)row * nchunks * kTopkSegCap;
+  const int tpc = kThreads / nchunks;  // nchunks <= kThreads
+  const int gc = threadIdx.x / tpc, j0 = threadIdx.x % tpc;
+  const int2* sg = segs + (size_t)min(gc, nchunks - 1) * kTopkSegCap;
+  constexpr int kSpec = 8;
+  int2 pre[kSpec];
+#pragma unroll
+  for (int u = 0; u < kSpec; u++) {
+    const int j = j0 + u * tpc;
+    pre[u] = j < kTopkSegCap ? sg[j] : make_int2(0, 0);
+  }
+  // Offsets of the candidate segments.
   int n;
   bool overflow;
   {
@@ -389,14 +407,18 @@ __global__ __launch_bounds__(kThreads) void topk_select(const float* __restrict_
     overflow = __syncthreads_or(v > kTopkSegCap) != 0;
   }
   if (n >= k && !overflow) {
-    const int2* segs = cand + (size_t)row * nchunks * kTopkSegCap;
     if (n <= kLdsCap) {
-      // tpc threads per chunk copy its segment to the LDS slots off[c]...
-      const int tpc = nchunks >= kThreads ? 1 : kThreads / nchunks;
-      for (int c = threadIdx.x / tpc; c < nchunks; c += kThreads / tpc) {
-        const int2* sg = segs + (size_t)c * kTopkSegCap;
-        const int o = off[c], cnt = off[c + 1] - off[c];
-        for (int j = threadIdx.x % tpc; j < cnt; j += tpc) {
+      if (gc < nchunks) {
+        const int o = off[gc], cnt = off[gc + 1] - off[gc];
+#pragma unroll
+        for (int u = 0; u < kSpec; u++) {
+          const int j = j0 + u * tpc;
+          if (j < cnt) {
+            lpos[o + j] = pre[u].x;
+            lkey[o + j] = (uint32_t)pre[u].y;
+          }
+        }
+        for (int j = j0 + kSpec * tpc; j < cnt; j += tpc) {
           const int2 e = sg[j];
           lpos[o + j] = e.x;
           lkey[o + j] = (uint32_t)e.y;
