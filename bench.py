@@ -9,10 +9,14 @@ the 128K-context decode (B=4, kv_len=131072, 64x128 bf16 indexer, k=2048,
 16 layers, 32 q / 8 KV heads, dim 128, 1% needle keys), synthetic seeded
 inputs resident in HBM before the timed region starts.
 
-Prints one JSON line: tokens/s for the step, the attention kernel's
-achieved HBM GB/s against the 8 TB/s peak (HIP events recorded by the
-library around every attention launch inside the timed steps), and the CPU
-oracle timed on the host on a bounded sample of the same workload.
+Prints one JSON line: tokens/s for the step (K timed steps, nothing enqueued
+between them), the step's spread and its cold-cache time, and the roofline
+of the dominant kernel, the sparse-attention call: algorithmic bytes over
+its GPU time per call (back-to-back calls replayed from a HIP graph between
+one event pair), warm and with the caches evicted before each call, plus the
+HBM traffic rocprofv3 measured for it; per-kernel times; a dense-gather run
+of the same call (k = kv_len) for the speedup; and the CPU oracle timed on
+one pinned host core on a bounded sample of the same workload.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--config decode128k]
 """
@@ -64,10 +68,25 @@ def algorithmic_bytes(wl):
     return {"index_score": index_score, "topk": topk, "sparse_attn": attn}
 
 
+def host_cpu():
+    """Host core count available to this process and the CPU model."""
+    model = ""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return len(os.sched_getaffinity(0)), model
+
+
 def cpu_baseline(wl, X, budget_s=12.0):
     """The oracle's decode step (all layers, one indexer pass) on host copies of
-    the same inputs, single-threaded, one batch element per call, cycling over
-    the batch until the time budget is spent (at least one call)."""
+    the same inputs, single-threaded and pinned to one core, one batch element
+    per call, cycling over the batch until the time budget is spent (at least
+    one call). For a chunk (T > 1) each call is one query of the chunk (T = 1
+    with that query's visible length), queries taken evenly over the chunk."""
     import oracle
     from token_sparse_attention_clsa_amd import inputs as inp
 
@@ -75,30 +94,48 @@ def cpu_baseline(wl, X, budget_s=12.0):
     for b in range(wl.B):
         memo = {}  # layers share one cache: copy each distinct tensor once
 
-        def sl(t):
+        def sl(t, tq=None):
             if t is None:
                 return None
-            if id(t) not in memo:
-                memo[id(t)] = inp.raw(t[b:b + 1])
-            return memo[id(t)]
+            key = (id(t), tq)
+            if key not in memo:
+                memo[key] = inp.raw(t[b:b + 1] if tq is None else t[b:b + 1, tq:tq + 1])
+            return memo[key]
 
-        host.append(([sl(t) for t in X.q], [sl(t) for t in X.k_cache], [sl(t) for t in X.v_cache],
-                     [sl(t) for t in X.q_idx], [sl(t) for t in X.k_idx], [sl(t) for t in X.w]))
+        host.append(sl)
+    queries = [None] if wl.T == 1 else [int(i * (wl.T - 1) / 15) for i in range(16)]
+    n_cores, model = host_cpu()
+    old_aff = os.sched_getaffinity(0)
+    os.sched_setaffinity(0, {min(old_aff)})
     done, t_total = 0, 0.0
-    while done == 0 or t_total < budget_s:
-        q, kc, vc, qi, ki, w = host[done % wl.B]
-        t0 = time.perf_counter()
-        oracle.decode_step(wl.layer_src, q, kc, vc, wl.dtype, qi, ki, w, wl.idx_dtype, wl.kv_len, wl.k)
-        t_total += time.perf_counter() - t0
-        done += 1
+    try:
+        while done == 0 or t_total < budget_s:
+            sl = host[done % wl.B]
+            tq = queries[(done // wl.B) % len(queries)]
+            kv = wl.kv_len if tq is None else wl.kv_len - wl.T + tq + 1
+            args = ([sl(t, tq) for t in X.q], [sl(t) for t in X.k_cache], [sl(t) for t in X.v_cache],
+                    [sl(t, tq) for t in X.q_idx], [sl(t) for t in X.k_idx], [sl(t, tq) for t in X.w])
+            t0 = time.perf_counter()
+            oracle.decode_step(wl.layer_src, args[0], args[1], args[2], wl.dtype, args[3], args[4], args[5],
+                               wl.idx_dtype, kv, wl.k)
+            t_total += time.perf_counter() - t0
+            done += 1
+            if done >= 64 * len(queries) * wl.B:
+                break
+    finally:
+        os.sched_setaffinity(0, old_aff)
+    what = ("single-batch-element decode steps" if wl.T == 1 else
+            f"single-query steps (16 queries spread over the {wl.T}-query chunk, each with its visible length)")
     return {
-        "value": done * wl.T / t_total,
+        "value": done / t_total,
         "unit": "tokens/s",
         "cores": 1,
         "kind": "oracle",
-        "sample": f"{done} single-batch-element decode steps ({wl.n_layers} layers, "
-                  f"{len(wl.f_layers)} indexer pass, kv_len {wl.kv_len}) of the same inputs, "
-                  f"{t_total:.1f} s of single-threaded CPU time",
+        "sample": f"{done} {what} ({wl.n_layers} layers, {len(wl.f_layers)} indexer pass, "
+                  f"kv_len {wl.kv_len}) of the same inputs, {t_total:.1f} s of CPU time on one "
+                  f"pinned core",
+        "host_cores": n_cores,
+        "host_cpu": model,
     }
 
 
@@ -246,6 +283,57 @@ def main():
                                                        ws=attn_ws))
     alg = algorithmic_bytes(wl)
     attn_gbs = alg["sparse_attn"] / (us_attn * 1e-6) / 1e9
+
+    # Cold figures: a 1 GiB fill before each timed call (or step) evicts the
+    # L2s and the 256 MB Infinity Cache; the fill also keeps the GPU busy while
+    # the host enqueues the event pair and the call, so the pair brackets GPU
+    # time only. Median over the repetitions.
+    scratch = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+
+    def cold_us(fn, reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ts = []
+        for i in range(reps + 2):
+            scratch.fill_(float(i))
+            a.record()
+            fn(i)
+            b.record()
+            torch.cuda.synchronize()
+            if i >= 2:
+                ts.append(a.elapsed_time(b) * 1e3)
+        return statistics.median(ts)
+
+    us_attn_cold = cold_us(lambda i: clsa.sparse_attn(X.q[i % n], X.k_cache[i % n], X.v_cache[i % n], idx,
+                                                      kv_len=wl.kv_len, out=out[i % n], lse=lse[i % n],
+                                                      ws=attn_ws), 20)
+    us_step_cold = cold_us(lambda i: step.run(), 10)
+
+    # Per-step spread: one event before each of K steps (none between kernels).
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
+    torch.cuda.synchronize()
+    evs[0].record()
+    for i in range(K):
+        step.run()
+        evs[i + 1].record()
+    torch.cuda.synchronize()
+    per_step = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(K))
+    pct = lambda f: per_step[min(K - 1, int(f * K))]
+
+    # Speedup context: the same attention call over every visible position
+    # (idx = 0..kv_len-1, a dense gather), decode only.
+    dense = None
+    if wl.T == 1:
+        idx_all = torch.arange(wl.kv_len, dtype=torch.int32, device="cuda").expand(wl.B, 1, wl.kv_len).contiguous()
+        ws_all = torch.empty(max(256, clsa.workspace_bytes(1, B=wl.B, T=1, Hq=wl.Hq, Hkv=wl.Hkv, D=wl.D,
+                                                           k=wl.kv_len)), dtype=torch.uint8, device="cuda")
+        us_dense = per_launch_us(lambda i: clsa.sparse_attn(X.q[0], X.k_cache[0], X.v_cache[0], idx_all,
+                                                            kv_len=wl.kv_len, out=out[0], lse=lse[0],
+                                                            ws=ws_all))
+        dense_bytes = wl.B * wl.kv_len * wl.Hkv * wl.D * (2 if wl.dtype == 1 else 4) * 2
+        dense = {"k": wl.kv_len, "us": us_dense, "gbs": dense_bytes / (us_dense * 1e-6) / 1e9,
+                 "speedup_sparse_vs_dense": us_dense / us_attn}
+        del idx_all, ws_all
+    del scratch
     step_bytes = len(wl.f_layers) * (alg["index_score"] + alg["topk"]) + n * alg["sparse_attn"]
     f_layers = wl.f_layers
 
@@ -290,7 +378,11 @@ def main():
                     "unit": "TFLOP/s", "frac": attn_tflops / MFMA_BF16_PEAK_TFLOPS, "traffic": None}
     split_kernel = "attn_split_mfma" if wl.dtype == 1 else "attn_split_kernel"
     roofline.update({"kernel": f"sparse_attn call ({split_kernel} + attn_combine_kernel)",
-                     "bytes_per_launch": alg["sparse_attn"], "avg_launch_us": us_attn})
+                     "bytes_per_launch": alg["sparse_attn"], "avg_launch_us": us_attn,
+                     "cold_launch_us": us_attn_cold})
+    if wl.T == 1:
+        cold_gbs = alg["sparse_attn"] / (us_attn_cold * 1e-6) / 1e9
+        roofline.update({"cold_achieved": cold_gbs, "cold_frac": cold_gbs / HBM_PEAK_GBS})
 
     tokens_per_step = wl.B * wl.T
     result = {
@@ -324,6 +416,9 @@ def main():
             "index_score_gbs": alg["index_score"] / (us_index * 1e-6) / 1e9,
         },
         "ms_per_step_events": ms_per_step_events,
+        "ms_per_step_p10_p50_p90": [pct(0.1), pct(0.5), pct(0.9)],
+        "ms_per_step_cold": us_step_cold * 1e-3,
+        "dense_gather_context": dense,
         "ms_per_step_graph_replay": graph_ms,
     }
     if comparator is not None:
