@@ -281,6 +281,15 @@ def main():
     us_attn = per_launch_us(lambda i: clsa.sparse_attn(X.q[i % n], X.k_cache[i % n], X.v_cache[i % n], idx,
                                                        kv_len=wl.kv_len, out=out[i % n], lse=lse[i % n],
                                                        ws=attn_ws))
+    # Cache append of the step's new tokens (rows kv_len-T .. kv_len-1 written
+    # again with copies of themselves, so the caches do not change).
+    pos = wl.kv_len - wl.T
+    new_rows = [X.k_cache[0][:, pos:wl.kv_len].clone(), X.v_cache[0][:, pos:wl.kv_len].clone(),
+                X.k_idx[f0][:, pos:wl.kv_len].clone()]
+    us_append = per_launch_us(lambda i: clsa.cache_append(new_rows[0], new_rows[1], X.k_cache[0],
+                                                          X.v_cache[0], pos, new_rows[2], X.k_idx[f0]))
+    del new_rows
+
     alg = algorithmic_bytes(wl)
     attn_gbs = alg["sparse_attn"] / (us_attn * 1e-6) / 1e9
 
@@ -413,6 +422,7 @@ def main():
             "sparse_attn": us_attn,
             "index_score": us_index,
             "topk": us_topk,
+            "cache_append": us_append,
             "index_score_gbs": alg["index_score"] / (us_index * 1e-6) / 1e9,
         },
         "ms_per_step_events": ms_per_step_events,

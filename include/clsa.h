@@ -236,6 +236,25 @@ int clsa_block_paged_attn(const void* q, const void* k_cache,
                           int Hq, int Hkv, int D, int kv_len, int L_cap,
                           float scale, void* stream);
 
+/*
+ * Appends T new tokens per batch element to the caches: every extra token of
+ * context adds a K and a V row (CLSA article, opening section), written once
+ * into the cache that all cross-decoder layers share (CLSA article,
+ * "Comment CLSA fonctionne"), together with the token's indexer key.
+ *   k_new, v_new  [B, T, Hkv, D]  dtype (F32 or BF16)  ->  k_cache, v_cache
+ *                 [B, L_cap, Hkv, D], rows pos .. pos + T - 1
+ *   kidx_new      [B, T, D_I]     idx_dtype            ->  k_idx [B, L_cap, D_I]
+ * kidx_new and k_idx are both NULL (no indexer keys) or both set. Bytes are
+ * copied unchanged; rows outside [pos, pos + T) are not touched. Needs
+ * pos >= 0 and pos + T <= L_cap; sources must not overlap destinations. The
+ * caller owns every buffer; one launch on `stream`, no workspace. Pointers
+ * must be 16-byte aligned.
+ */
+int clsa_cache_append(const void* k_new, const void* v_new, void* k_cache,
+                      void* v_cache, int dtype, const void* kidx_new,
+                      void* k_idx, int idx_dtype, int B, int T, int Hkv,
+                      int D, int D_I, int pos, int L_cap, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

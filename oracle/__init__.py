@@ -12,6 +12,7 @@ from .oracle import (  # noqa: F401
     block_attn,
     block_union,
     build,
+    cache_append,
     decode,
     decode_step,
     index_score,

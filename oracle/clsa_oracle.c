@@ -14,8 +14,8 @@
  * exp and log from libm.
  *
  * Sources (pages; section names as they appear there):
- *  [CLSA]  SeventNews article on "CLSA: You Only Index Once",
- *          section "Comment CLSA fonctionne".
+ *  [CLSA]  SeventNews article on "CLSA: You Only Index Once", its opening
+ *          section and section "Comment CLSA fonctionne".
  *  [IC]    gist.science summary of "IndexCache: Accelerating Sparse Attention
  *          via Cross-Layer Index Reuse", sections "1. Problématique" and
  *          "2. Méthodologie : IndexCache".
@@ -494,5 +494,27 @@ int orc_block_attn(const void* q, const void* kc, const void* vc, int dtype,
   }
   free(z);
   free(sel);
+  return 0;
+}
+
+/*
+ * Cache append: row t of every batch element of src [B, T, row_bytes] is
+ * copied byte for byte to row pos + t of dst [B, L_cap, row_bytes]; every
+ * other row of dst is left as it is. One call per cache tensor (K, V,
+ * indexer keys). Each new token of context adds its keys and values to the
+ * stored cache ([CLSA] opening section), a cache written once and shared by
+ * the cross-decoder layers ([CLSA] "Comment CLSA fonctionne").
+ * Pinned by: appending T rows at once equals T single-row appends; rows
+ * outside [pos, pos + T) unchanged; a decode step over a cache rebuilt by
+ * appending its last rows equals the step over the original cache.
+ */
+int orc_cache_append(const unsigned char* src, unsigned char* dst, int B, int T,
+                     long row_bytes, int pos, int L_cap) {
+  if (B < 1 || T < 1 || row_bytes < 1 || pos < 0 || (long)pos + T > L_cap) return -1;
+  for (int b = 0; b < B; b++)
+    for (int t = 0; t < T; t++)
+      for (long i = 0; i < row_bytes; i++)
+        dst[((size_t)b * L_cap + pos + t) * (size_t)row_bytes + i] =
+            src[((size_t)b * T + t) * (size_t)row_bytes + i];
   return 0;
 }

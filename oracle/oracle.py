@@ -53,6 +53,7 @@ def _load():
             )
             lib.orc_block_union.argtypes = [P, I, I, I, I, I, I, P, P]
             lib.orc_block_attn.argtypes = [P, P, P, I, P, P, I, P, P] + [I] * 7 + [D]
+            lib.orc_cache_append.argtypes = [P, P, I, I, ctypes.c_long, I, I]
             for f in (
                 lib.orc_decode,
                 lib.orc_index_score,
@@ -61,6 +62,7 @@ def _load():
                 lib.orc_decode_step,
                 lib.orc_block_union,
                 lib.orc_block_attn,
+                lib.orc_cache_append,
             ):
                 f.restype = ctypes.c_int
             lib.orc_decode.restype = None
@@ -205,3 +207,18 @@ def block_attn(q, k_cache, v_cache, dtype, kv_indptr, kv_indices, block, kv_len,
                                 block, _p(out), _p(lse), B, T, Hq, Hkv, D, kv_len, L_cap, float(scale))
     _check(rc, "block_attn")
     return out, lse
+
+
+def cache_append(new, cache, pos):
+    """Cache with the T rows of new [B, T, ...] written at rows pos .. pos+T-1
+    of cache [B, L_cap, ...] (same trailing shape and element type). Returns a
+    new array; the input cache is not modified."""
+    new = np.ascontiguousarray(new)
+    out = np.array(cache, copy=True, order="C")
+    if new.dtype != out.dtype or new.shape[0] != out.shape[0] or new.shape[2:] != out.shape[2:]:
+        raise TypeError(f"cache_append: new {new.shape} {new.dtype} vs cache {out.shape} {out.dtype}")
+    B, T = new.shape[:2]
+    row_bytes = int(np.prod(new.shape[2:], dtype=np.int64)) * new.dtype.itemsize
+    rc = _load().orc_cache_append(_p(new), _p(out), B, T, row_bytes, int(pos), out.shape[1])
+    _check(rc, "cache_append")
+    return out

@@ -24,7 +24,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = clsa.declared_symbols()
-    assert len(names) == 11
+    assert len(names) == 12
     for required in ("clsa_index_score", "clsa_topk", "clsa_sparse_attn", "clsa_decode_step"):
         assert required in names
     raw = ctypes.CDLL(binding.LIB_PATH)
@@ -149,3 +149,24 @@ def test_block_calls_reject(lib):
     assert lib.clsa_block_union_build(FAKE, 1, 1, 4, 100, 64, 8, FAKE, FAKE, FAKE, 0, None) == -3
     assert lib.clsa_block_paged_attn(FAKE, FAKE, FAKE, 0, FAKE, FAKE, 64, FAKE, None, 1, 1, 32, 8, 128,
                                      100, 100, 0.0, None) == -2   # f32 comparator not built
+
+
+def test_cache_append_rejects(lib):
+    A, Bp, C, Dp = FAKE, FAKE + (1 << 24), FAKE + (1 << 26), FAKE + (1 << 28)
+    E, Fp = FAKE + (1 << 30), FAKE + (1 << 31)
+
+    def call(k_new=A, v_new=Bp, kc=C, vc=Dp, dtype=1, ki_new=None, ki=None, idt=1, B=2, T=1, Hkv=8,
+             D=128, D_I=128, pos=10, cap=64):
+        return lib.clsa_cache_append(k_new, v_new, kc, vc, dtype, ki_new, ki, idt, B, T, Hkv, D, D_I, pos,
+                                     cap, None)
+
+    assert call(k_new=None) == -1
+    assert call(ki_new=E) == -1 and b"both" in lib.clsa_last_error()     # indexer keys without a cache
+    assert call(pos=64) == -1                                             # past L_cap
+    assert call(pos=62, T=3) == -1
+    assert call(pos=-1) == -1
+    assert call(dtype=2) == -1                                            # fp8 K/V caches not supported
+    assert call(ki_new=E, ki=Fp, idt=7) == -1
+    assert call(k_new=A + 4) == -1 and b"misaligned" in lib.clsa_last_error()
+    assert call(k_new=C + 4096) == -1 and b"overlap" in lib.clsa_last_error()  # source inside a cache
+    assert call(B=0) == -1

@@ -13,6 +13,7 @@ from .binding import (  # noqa: F401
     DecodeStep,
     block_paged_attn,
     block_union_build,
+    cache_append,
     decode_step,
     declared_symbols,
     index_score,

@@ -82,6 +82,7 @@ def load() -> ctypes.CDLL:
         "clsa_decode_step": (I, [ctypes.POINTER(StepDesc), P, SZ, P]),
         "clsa_block_union_build": (I, [P] + [I] * 6 + [P, P, P, SZ, P]),
         "clsa_block_paged_attn": (I, [P, P, P, I, P, P, I, P, P] + [I] * 7 + [F, P]),
+        "clsa_cache_append": (I, [P, P, P, P, I, P, P] + [I] * 8 + [P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -316,3 +317,27 @@ def block_paged_attn(q, k_cache, v_cache, kv_indptr, kv_indices, block: int, kv_
                                       B, T, Hq, Hkv, D, kv_len, L_cap, float(scale), _stream())
     _check(rc, "clsa_block_paged_attn")
     return out, lse
+
+
+def cache_append(k_new, v_new, k_cache, v_cache, pos: int, kidx_new=None, k_idx=None):
+    """clsa_cache_append: writes the T new tokens of every batch element at
+    cache rows pos .. pos + T - 1 (K, V and, when given, indexer keys)."""
+    _dev(k_new, "k_new", (torch.float32, torch.bfloat16))
+    B, T, Hkv, D = k_new.shape
+    _dev(v_new, "v_new", (k_new.dtype,), (B, T, Hkv, D))
+    L_cap = k_cache.shape[1]
+    _dev(k_cache, "k_cache", (k_new.dtype,), (B, L_cap, Hkv, D))
+    _dev(v_cache, "v_cache", (k_new.dtype,), (B, L_cap, Hkv, D))
+    D_I, idt = 0, F32
+    if (kidx_new is None) != (k_idx is None):
+        raise ValueError("kidx_new and k_idx go together")
+    if k_idx is not None:
+        _dev(kidx_new, "kidx_new", _DT)
+        D_I = kidx_new.shape[2]
+        _dev(kidx_new, "kidx_new", shape=(B, T, D_I))
+        _dev(k_idx, "k_idx", (kidx_new.dtype,), (B, L_cap, D_I))
+        idt = _DT[kidx_new.dtype]
+    rc = load().clsa_cache_append(_ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache),
+                                  _DT[k_new.dtype], _ptr(kidx_new), _ptr(k_idx), idt, B, T, Hkv, D,
+                                  D_I, pos, L_cap, _stream())
+    _check(rc, "clsa_cache_append")

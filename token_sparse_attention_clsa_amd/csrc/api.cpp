@@ -2,8 +2,9 @@
 //
 // Every entry point validates all of its arguments before it enqueues
 // anything, carves the caller's workspace, and enqueues the kernels of
-// index_score.hip, topk.hip, sparse_attn.hip and block_union.hip on the
-// caller's stream. Nothing here allocates device memory or synchronises.
+// cache_append.hip, index_score.hip, topk.hip, sparse_attn.hip,
+// block_union.hip and block_attn.hip on the caller's stream. Nothing here
+// allocates device memory or synchronises.
 #include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
@@ -355,6 +356,47 @@ int clsa_block_paged_attn(const void* q, const void* k_cache, const void* v_cach
   return launch_block_paged_attn(q, k_cache, v_cache, dtype, kv_indptr, kv_indices, block, out, lse,
                                  B, T, Hq, Hkv, D, kv_len, L_cap, scale,
                                  static_cast<hipStream_t>(stream));
+}
+
+int clsa_cache_append(const void* k_new, const void* v_new, void* k_cache, void* v_cache, int dtype,
+                      const void* kidx_new, void* k_idx, int idx_dtype, int B, int T, int Hkv, int D,
+                      int D_I, int pos, int L_cap, void* stream) {
+  if (!k_new || !v_new || !k_cache || !v_cache)
+    return set_error(CLSA_ERR_INVALID_ARG, "cache_append: null pointer");
+  if ((kidx_new == nullptr) != (k_idx == nullptr))
+    return set_error(CLSA_ERR_INVALID_ARG, "cache_append: kidx_new and k_idx must both be set or both NULL");
+  if (B < 1 || T < 1 || Hkv < 1 || D < 1 || (k_idx && D_I < 1))
+    return set_error(CLSA_ERR_INVALID_ARG, "cache_append: B=%d T=%d Hkv=%d D=%d D_I=%d", B, T, Hkv, D, D_I);
+  if (pos < 0 || (long)pos + T > L_cap)
+    return set_error(CLSA_ERR_INVALID_ARG, "cache_append: rows [%d, %ld) outside L_cap=%d", pos,
+                     (long)pos + T, L_cap);
+  if ((long)B * T > 0x7fffffffL)
+    return set_error(CLSA_ERR_UNSUPPORTED, "cache_append: B*T=%ld", (long)B * T);
+  if (dtype != CLSA_F32 && dtype != CLSA_BF16)
+    return set_error(CLSA_ERR_INVALID_ARG, "cache_append: unknown dtype %d", dtype);
+  if (k_idx && idx_dtype != CLSA_F32 && idx_dtype != CLSA_BF16 && idx_dtype != CLSA_FP8_E4M3FN)
+    return set_error(CLSA_ERR_INVALID_ARG, "cache_append: unknown indexer dtype %d", idx_dtype);
+  if (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
+      (k_idx && (!aligned(kidx_new, 16) || !aligned(k_idx, 16))))
+    return set_error(CLSA_ERR_INVALID_ARG, "cache_append: misaligned pointer");
+  const size_t kv_row = (size_t)Hkv * D * (dtype == CLSA_F32 ? 4 : 2);
+  const size_t ki_row = k_idx ? (size_t)D_I * (idx_dtype == CLSA_F32 ? 4 : idx_dtype == CLSA_BF16 ? 2 : 1) : 0;
+  AppendJob jobs[3] = {{static_cast<const char*>(k_new), static_cast<char*>(k_cache), kv_row},
+                       {static_cast<const char*>(v_new), static_cast<char*>(v_cache), kv_row},
+                       {static_cast<const char*>(kidx_new), static_cast<char*>(k_idx), ki_row}};
+  const int n_jobs = k_idx ? 3 : 2;
+  const size_t rows = (size_t)B * T;
+  for (int i = 0; i < n_jobs; i++) {
+    const size_t src_bytes = rows * jobs[i].row_bytes;
+    for (int o = 0; o < n_jobs; o++) {
+      const char* s0 = jobs[i].src;
+      const char* d0 = jobs[o].dst;
+      const size_t d_bytes = (size_t)B * L_cap * jobs[o].row_bytes;
+      if (s0 < d0 + d_bytes && d0 < s0 + src_bytes)
+        return set_error(CLSA_ERR_INVALID_ARG, "cache_append: a source overlaps a destination");
+    }
+  }
+  return launch_cache_append(jobs, n_jobs, B, T, pos, L_cap, static_cast<hipStream_t>(stream));
 }
 
 }  // extern "C"

@@ -7,6 +7,17 @@
 
 namespace clsa {
 
+// ---- cache append ------------------------------------------------------------
+// One tensor to append: B*T rows of row_bytes from src (row r = b*T + t) to
+// dst row b*L_cap + pos + t.
+struct AppendJob {
+  const char* src;
+  char* dst;
+  size_t row_bytes;
+};
+int launch_cache_append(const AppendJob* jobs, int n_jobs, int B, int T, int pos, int L_cap,
+                        hipStream_t stream);
+
 // ---- indexer score ---------------------------------------------------------
 int launch_index_score(const void* q_idx, const void* k_idx, int idx_dtype, const float* w,
                        float* scores, int B, int T, int H_I, int D_I, int kv_len, int L_cap,
