@@ -227,6 +227,28 @@ def main():
         graph_ms = (time.perf_counter() - t2) * 1e3 / K
         print(f"[bench] graph replay: {graph_ms * 1e3:.1f} us/step", file=sys.stderr, flush=True)
 
+    # The same step with a per-query count of kept positions (the dynamic-k
+    # reading), counts drawn uniformly from [k/4, k] (seeded): GPU time of K
+    # back-to-back steps between one event pair (the wall clock of the first
+    # pass after this step's warmup has shown a one-off stall of ~16 ms before
+    # the GPU starts, outside the steps themselves).
+    gk = torch.Generator().manual_seed(17)
+    kpq = torch.randint(wl.k // 4, wl.k + 1, (wl.B, wl.T), generator=gk, dtype=torch.int32).to("cuda")
+    step_dk = clsa.DecodeStep(wl.layer_src, X.q, X.k_cache, X.v_cache, X.q_idx, X.k_idx, X.w, wl.k,
+                              kv_len=wl.kv_len, k_per_query=kpq)
+    for _ in range(W):
+        step_dk.run()
+    torch.cuda.synchronize()
+    e3a, e3b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e3a.record()
+    for _ in range(K):
+        step_dk.run()
+    e3b.record()
+    torch.cuda.synchronize()
+    dynamic_k = {"k_per_query": f"uniform [{wl.k // 4}, {wl.k}]", "mean_k": float(kpq.float().mean()),
+                 "ms_per_step_events": e3a.elapsed_time(e3b) / K}
+    del step_dk
+
     # Per-kernel averages: R back-to-back calls of one entry point, same
     # shapes and inputs as the step. The R calls are captured once in a HIP
     # graph and replayed between one event pair on the replay stream, so the
@@ -429,6 +451,7 @@ def main():
         "ms_per_step_p10_p50_p90": [pct(0.1), pct(0.5), pct(0.9)],
         "ms_per_step_cold": us_step_cold * 1e-3,
         "dense_gather_context": dense,
+        "dynamic_k": dynamic_k,
         "ms_per_step_graph_replay": graph_ms,
     }
     if comparator is not None:

@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define CLSA_ABI_VERSION 1
+#define CLSA_ABI_VERSION 2
 
 /* Status codes returned by every entry point. */
 enum clsa_status {
@@ -130,6 +130,20 @@ int clsa_topk(const float* scores, int B, int T, int kv_len, int k,
               int32_t* idx, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * clsa_topk with a per-query count: query (b, t) keeps its
+ * k_per_query[b, t] best positions (clamped to [0, k]) and the remaining
+ * slots of its k-wide row hold -1. The pages keep k fixed and name a k
+ * chosen by the indexer layer as the open extension (CLSA article, "Le
+ * coût : limites de compatibilité"; "Ce que cela signifie pour
+ * l'inférence sur longs contextes"); the rule that picks each count is the
+ * caller's. k_per_query: device int32 [B, T], or
+ * NULL for k everywhere. Same workspace, ordering and errors as clsa_topk.
+ */
+int clsa_topk_vark(const float* scores, int B, int T, int kv_len, int k,
+                   const int32_t* k_per_query, int32_t* idx, void* ws,
+                   size_t ws_bytes, void* stream);
+
+/*
  * Gathered sparse attention over the selected tokens (IndexCache summary,
  * "1. Problématique": main attention over the k selected tokens, O(Lk);
  * CLSA article, "Comment CLSA fonctionne": every layer after the indexer
@@ -194,6 +208,10 @@ typedef struct clsa_step_desc {
    * events[4l+2] before attention and events[4l+3] after it (S layers record
    * the first three back to back). */
   void* const* events;
+  /* Optional per-query counts: NULL (every query keeps k positions), or a
+   * device int32 [B, T]; query (b, t) keeps its k_per_query[b, t] best
+   * positions (clamped to [0, k]) as in clsa_topk_vark. */
+  const int32_t* k_per_query;
 } clsa_step_desc;
 
 /* Workspace bytes needed by clsa_decode_step for this descriptor (0 if the

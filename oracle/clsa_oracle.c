@@ -228,10 +228,14 @@ static int orc_cmp_long(const void* a, const void* b) {
 
 /*
  * For each (b,t): sort the visible positions by (score desc, position asc),
- * keep the first min(k, visible), return them in ascending position order,
- * pad with -1 to k.  scores [B,T,kv_len] double, idx [B,T,k] int32.
+ * keep the first min(k_bt, visible), return them in ascending position
+ * order, pad with -1 to k.  scores [B,T,kv_len] double, idx [B,T,k] int32.
+ * k_bt = k, or with k_rows [B,T] (the per-query count of the query-dependent
+ * k reading; [CLSA] "Le coût : limites de compatibilité") k_rows[b,t]
+ * clamped to [0, k].
  */
-int orc_topk(const double* scores, int B, int T, int kv_len, int k, int32_t* idx) {
+int orc_topk(const double* scores, int B, int T, int kv_len, int k, const int32_t* k_rows,
+             int32_t* idx) {
   if (B < 1 || T < 1 || kv_len < T || k < 1) return -1;
   orc_cand* c = (orc_cand*)malloc(sizeof(orc_cand) * (size_t)kv_len);
   long* chosen = (long*)malloc(sizeof(long) * (size_t)k);
@@ -249,7 +253,13 @@ int orc_topk(const double* scores, int B, int T, int kv_len, int k, int32_t* idx
         c[s].pos = s;
       }
       qsort(c, (size_t)vis, sizeof(orc_cand), orc_cmp_rank);
-      long n = vis < k ? vis : k;
+      long kb = k;
+      if (k_rows) {
+        kb = k_rows[(size_t)b * T + t];
+        if (kb < 0) kb = 0;
+        if (kb > k) kb = k;
+      }
+      long n = vis < kb ? vis : kb;
       for (long j = 0; j < n; j++) chosen[j] = c[j].pos;
       qsort(chosen, (size_t)n, sizeof(long), orc_cmp_long);
       int32_t* out = idx + ((size_t)b * T + t) * k;
@@ -350,7 +360,8 @@ int orc_sparse_attn(const void* q, const void* kc, const void* vc, int dtype,
  * buffer idx_out [B,T,k]. Every layer l then attends with the buffer as the
  * nearest F layer at or before l left it.
  * Per-layer arrays hold host pointers to host buffers (F-layer indexer
- * inputs may be NULL for S layers). out[l] [B,T,Hq,D] double, lse[l]
+ * inputs may be NULL for S layers). k_rows (may be NULL) gives each query
+ * its own count, as in orc_topk. out[l] [B,T,Hq,D] double, lse[l]
  * [B,T,Hq] double. n_indexer_calls (may be NULL) receives how many times
  * the indexer ran. Returns -1 for an invalid layer map.
  */
@@ -361,7 +372,8 @@ int orc_decode_step(int n_layers, const int32_t* layer_src,
                     const float* const* w, int idx_dtype, int32_t* idx_out,
                     double* const* out, double* const* lse, int B, int T,
                     int Hq, int Hkv, int D, int H_I, int D_I, int kv_len,
-                    int L_cap, int k, double scale, int* n_indexer_calls) {
+                    int L_cap, int k, const int32_t* k_rows, double scale,
+                    int* n_indexer_calls) {
   if (n_layers < 1 || layer_src[0] != 0) return -1;
   int last_f = -1;
   for (int l = 0; l < n_layers; l++) {
@@ -375,7 +387,7 @@ int orc_decode_step(int n_layers, const int32_t* layer_src,
     if (layer_src[l] == l) {
       int rc = orc_index_score(q_idx[l], k_idx[l], idx_dtype, w[l], scores, NULL,
                                B, T, H_I, D_I, kv_len, L_cap);
-      if (rc == 0) rc = orc_topk(scores, B, T, kv_len, k, idx_out);
+      if (rc == 0) rc = orc_topk(scores, B, T, kv_len, k, k_rows, idx_out);
       if (rc) {
         free(scores);
         return rc;

@@ -46,10 +46,10 @@ def _load():
             P, I, D = ctypes.c_void_p, ctypes.c_int, ctypes.c_double
             lib.orc_decode.argtypes = [P, I, ctypes.c_long, P]
             lib.orc_index_score.argtypes = [P, P, I, P, P, P] + [I] * 6
-            lib.orc_topk.argtypes = [P, I, I, I, I, P]
+            lib.orc_topk.argtypes = [P, I, I, I, I, P, P]
             lib.orc_sparse_attn.argtypes = [P, P, P, I, P, I, P, P] + [I] * 7 + [D]
             lib.orc_decode_step.argtypes = (
-                [I, P, P, P, P, I, P, P, P, I, P, P, P] + [I] * 10 + [D, P]
+                [I, P, P, P, P, I, P, P, P, I, P, P, P] + [I] * 10 + [P, D, P]
             )
             lib.orc_block_union.argtypes = [P, I, I, I, I, I, I, P, P]
             lib.orc_block_attn.argtypes = [P, P, P, I, P, P, I, P, P] + [I] * 7 + [D]
@@ -114,15 +114,17 @@ def index_score(q_idx, k_idx, dtype, w, kv_len, with_bound=False):
     return (scores, bound) if with_bound else scores
 
 
-def topk(scores, k, kv_len=None):
-    """Top-k positions per (b,t). scores [B,T,kv_len] (any float dtype, taken exactly)."""
+def topk(scores, k, kv_len=None, k_rows=None):
+    """Top-k positions per (b,t). scores [B,T,kv_len] (any float dtype, taken exactly).
+    k_rows (optional int32 [B,T]): per-query count of kept positions, clamped to [0, k]."""
     scores = np.ascontiguousarray(scores, dtype=np.float64)
     B, T, L = scores.shape
     kv_len = L if kv_len is None else kv_len
     if kv_len != L:
         raise ValueError("topk: scores last dim must equal kv_len")
+    kr = None if k_rows is None else _c(np.asarray(k_rows).reshape(B, T), np.int32)
     idx = np.empty((B, T, k), np.int32)
-    _check(_load().orc_topk(_p(scores), B, T, kv_len, k, _p(idx)), "topk")
+    _check(_load().orc_topk(_p(scores), B, T, kv_len, k, _p(kr), _p(idx)), "topk")
     return idx
 
 
@@ -147,7 +149,7 @@ def sparse_attn(q, k_cache, v_cache, dtype, idx, kv_len, scale=0.0):
 
 
 def decode_step(layer_src, q, k_cache, v_cache, dtype, q_idx, k_idx, w, idx_dtype, kv_len, k,
-                scale=0.0):
+                scale=0.0, k_rows=None):
     """One step over len(layer_src) layers sharing routing.
 
     Per-layer lists of numpy arrays (indexer inputs may be None on S layers).
@@ -168,6 +170,7 @@ def decode_step(layer_src, q, k_cache, v_cache, dtype, q_idx, k_idx, w, idx_dtyp
     outs = [np.empty((B, T, Hq, D), np.float64) for _ in range(n)]
     lses = [np.empty((B, T, Hq), np.float64) for _ in range(n)]
     idx = np.empty((B, T, k), np.int32)
+    kr = None if k_rows is None else _c(np.asarray(k_rows).reshape(B, T), np.int32)
     calls = ctypes.c_int(0)
     VP = ctypes.c_void_p * n
 
@@ -176,7 +179,7 @@ def decode_step(layer_src, q, k_cache, v_cache, dtype, q_idx, k_idx, w, idx_dtyp
 
     rc = _load().orc_decode_step(
         n, _p(src), arr(qs), arr(ks), arr(vs), dtype, arr(qi), arr(ki), arr(ws), idx_dtype, _p(idx),
-        arr(outs), arr(lses), B, T, Hq, Hkv, D, H_I, D_I, kv_len, L_cap, k, float(scale),
+        arr(outs), arr(lses), B, T, Hq, Hkv, D, H_I, D_I, kv_len, L_cap, k, _p(kr), float(scale),
         ctypes.byref(calls),
     )
     _check(rc, "decode_step")

@@ -54,6 +54,7 @@ class StepDesc(ctypes.Structure):
         ("kv_len", I), ("L_cap", I), ("k", I),
         ("scale", F),
         ("events", ctypes.POINTER(P)),
+        ("k_per_query", P),
     ]
 
 
@@ -77,6 +78,7 @@ def load() -> ctypes.CDLL:
         "clsa_workspace_bytes": (SZ, [I] * 9),
         "clsa_index_score": (I, [P, P, I, P, P] + [I] * 6 + [P]),
         "clsa_topk": (I, [P, I, I, I, I, P, P, SZ, P]),
+        "clsa_topk_vark": (I, [P, I, I, I, I, P, P, P, SZ, P]),
         "clsa_sparse_attn": (I, [P, P, P, I, P, I, P, P] + [I] * 7 + [F, P, SZ, P]),
         "clsa_decode_step_workspace_bytes": (SZ, [ctypes.POINTER(StepDesc)]),
         "clsa_decode_step": (I, [ctypes.POINTER(StepDesc), P, SZ, P]),
@@ -156,8 +158,9 @@ def index_score(q_idx: torch.Tensor, k_idx: torch.Tensor, w: torch.Tensor, kv_le
 
 
 def topk(scores: torch.Tensor, k: int, out: Optional[torch.Tensor] = None,
-         ws: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """clsa_topk. scores [B,T,kv_len] f32 -> idx [B,T,k] int32 (ascending, -1 padded)."""
+         ws: Optional[torch.Tensor] = None, k_per_query: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """clsa_topk (clsa_topk_vark with k_per_query [B,T] int32).
+    scores [B,T,kv_len] f32 -> idx [B,T,k] int32 (ascending, -1 padded)."""
     _dev(scores, "scores", (torch.float32,))
     B, T, L = scores.shape
     if out is None:
@@ -166,8 +169,14 @@ def topk(scores: torch.Tensor, k: int, out: Optional[torch.Tensor] = None,
     need = workspace_bytes(OP_TOPK, B=B, T=T, kv_len=L, k=k)
     if ws is None:
         ws = _workspace(need, scores.device)
-    rc = load().clsa_topk(_ptr(scores), B, T, L, k, _ptr(out), _ptr(ws), ws.numel(), _stream())
-    _check(rc, "clsa_topk")
+    if k_per_query is None:
+        rc = load().clsa_topk(_ptr(scores), B, T, L, k, _ptr(out), _ptr(ws), ws.numel(), _stream())
+        _check(rc, "clsa_topk")
+    else:
+        _dev(k_per_query, "k_per_query", (torch.int32,), (B, T))
+        rc = load().clsa_topk_vark(_ptr(scores), B, T, L, k, _ptr(k_per_query), _ptr(out), _ptr(ws),
+                                   ws.numel(), _stream())
+        _check(rc, "clsa_topk_vark")
     return out
 
 
@@ -209,12 +218,13 @@ class DecodeStep:
     Per-layer lists: q, k_cache, v_cache; indexer lists q_idx, k_idx, w hold
     tensors on F layers and None on S layers. ``run()`` enqueues one step on
     torch's current stream; outputs live in ``self.out`` / ``self.lse`` and the
-    index cache in ``self.idx``.
+    index cache in ``self.idx``. ``k_per_query`` (int32 [B, T], optional) gives
+    each query its own count of kept positions (as clsa_topk_vark).
     """
 
     def __init__(self, layer_src: Sequence[int], q, k_cache, v_cache, q_idx, k_idx, w, k: int,
                  kv_len: Optional[int] = None, scale: float = 0.0, want_lse: bool = True,
-                 events: Optional[Sequence] = None):
+                 events: Optional[Sequence] = None, k_per_query: Optional[torch.Tensor] = None):
         n = len(layer_src)
         self.n = n
         dev = q[0].device
@@ -233,7 +243,9 @@ class DecodeStep:
                 _dev(q_idx[l], f"q_idx[{l}]", (q_idx[f0].dtype,), (B, T, H_I, D_I))
                 _dev(k_idx[l], f"k_idx[{l}]", (q_idx[f0].dtype,), (B, L_cap, D_I))
                 _dev(w[l], f"w[{l}]", (torch.float32,), (B, T, H_I))
-        self._keep = [q, k_cache, v_cache, q_idx, k_idx, w]
+        if k_per_query is not None:
+            _dev(k_per_query, "k_per_query", (torch.int32,), (B, T))
+        self._keep = [q, k_cache, v_cache, q_idx, k_idx, w, k_per_query]
         self.out = [torch.empty_like(q[l]) for l in range(n)]
         self.lse = [torch.empty((B, T, Hq), dtype=torch.float32, device=dev) for _ in range(n)] \
             if want_lse else None
@@ -261,7 +273,8 @@ class DecodeStep:
             self._lse if self._lse is not None else ctypes.POINTER(P)(),
             self._qi, self._ki, self._w, self.idx.data_ptr(),
             _DT[q[0].dtype], _DT[q_idx[f0].dtype], B, T, Hq, Hkv, D, H_I, D_I, kv_len, L_cap, k,
-            float(scale), self._ev if self._ev is not None else ctypes.POINTER(P)())
+            float(scale), self._ev if self._ev is not None else ctypes.POINTER(P)(),
+            None if k_per_query is None else k_per_query.data_ptr())
         lib = load()
         need = lib.clsa_decode_step_workspace_bytes(ctypes.byref(self.desc))
         if need == 0:

@@ -37,22 +37,27 @@ struct TopkBuffers {
   size_t counts_words, cand_words, spill_words;
 };
 TopkBuffers topk_buffers(int rows, int kv_len);
-int launch_topk(const float* scores, int B, int T, int kv_len, int k, int32_t* idx,
-                uint32_t* counts, int32_t* cand, int32_t* spill, hipStream_t stream);
+// k_rows: NULL, or a device int32 [B*T] of per-row counts (clamped to [0, k]).
+int launch_topk(const float* scores, int B, int T, int kv_len, int k, const int32_t* k_rows,
+                int32_t* idx, uint32_t* counts, int32_t* cand, int32_t* spill, hipStream_t stream);
 
 // ---- sparse attention --------------------------------------------------------
 // Buffer: partials [attn_partial_floats(...)] f32 (split states; unused when
 // the k entries are not split).
 struct AttnSplit {
   int splits, rows_per_split;
-  int waves_per_head;  // waves sharing one split of one KV head
+  int waves_per_head;     // waves sharing one split of one KV head
+  bool skip_empty_steps;  // bf16: skip 32-entry steps with no visible entry
 };
 AttnSplit attn_split(int B, int T, int Hkv, int k, bool mfma);
 size_t attn_partial_floats(int B, int T, int Hq, int Hkv, int k);
 bool sparse_attn_supported(int dtype, int Hq, int Hkv, int D);
+// skip_empty_steps: the index rows may end in long -1 tails (per-query
+// counts below k); bf16 then skips 32-entry steps with no visible entry.
 int launch_sparse_attn(const void* q, const void* kc, const void* vc, int dtype, const int32_t* idx,
                        int k, void* out, float* lse, int B, int T, int Hq, int Hkv, int D,
-                       int kv_len, int L_cap, float scale, float* partials, hipStream_t stream);
+                       int kv_len, int L_cap, float scale, float* partials, bool skip_empty_steps,
+                       hipStream_t stream);
 
 // ---- block union comparator ----------------------------------------------------
 size_t block_union_ws_bytes(int B, int kv_len, int block);

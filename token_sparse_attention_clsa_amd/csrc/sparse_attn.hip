@@ -330,7 +330,13 @@ __device__ __forceinline__ int vis_pos(const int32_t* irow, int e, int end, int 
   const int p = e < end ? irow[e] : -1;
   return (p >= 0 && p < vis) ? p : -1;
 }
-__device__ __forceinline__ void kv_issue(KvStep& f, const int32_t* irow, int e0, int end, int vis,
+// With SKIP, returns false and issues no load when none of the 32 entries
+// is visible (e.g. the -1 tail of a query that keeps fewer than k
+// positions); the result is uniform over the wave. Without SKIP the step is
+// always loaded (masked entries read row 0), which keeps the fixed-k code
+// free of the branch.
+template <bool SKIP>
+__device__ __forceinline__ bool kv_issue(KvStep& f, const int32_t* irow, int e0, int end, int vis,
                                          int col, int grp, const char* kb, const char* vb,
                                          size_t tok) {
   int kp[2], vp[2][4];
@@ -345,6 +351,9 @@ __device__ __forceinline__ void kv_issue(KvStep& f, const int32_t* irow, int e0,
   for (int tt = 0; tt < 2; tt++)
 #pragma unroll
     for (int r = 0; r < 4; r++) f.valid |= (vp[tt][r] >= 0 ? 1u : 0u) << (4 * tt + r);
+  if constexpr (SKIP) {
+    if (__ballot(f.valid != 0u) == 0) return false;
+  }
 #pragma unroll
   for (int tt = 0; tt < 2; tt++)
 #pragma unroll
@@ -356,6 +365,7 @@ __device__ __forceinline__ void kv_issue(KvStep& f, const int32_t* irow, int e0,
 #pragma unroll
     for (int r = 0; r < 4; r++)
       f.vf[tt][r] = *reinterpret_cast<const uint4*>(vb + (size_t)max(vp[tt][r], 0) * tok);
+  return true;
 }
 
 // Running state of one wave: O^T accumulators, max and sum of head col.
@@ -441,7 +451,7 @@ __device__ __forceinline__ void kv_consume(const KvStep& f, MfmaState& st, const
 // steps w, w + W, ... and the W states are merged through LDS before the
 // split's single state is written (W > 1 keeps many waves in flight with
 // few splits, so fewer states go through memory).
-template <int G, int W>
+template <int G, int W, bool SKIP>
 __global__ __launch_bounds__(kWave * kMaxWaves) void attn_split_mfma(
     const char* __restrict__ q, const char* __restrict__ kc, const char* __restrict__ vc,
     const int32_t* __restrict__ idx, int k, void* __restrict__ out, float* __restrict__ lse,
@@ -494,8 +504,8 @@ __global__ __launch_bounds__(kWave * kMaxWaves) void attn_split_mfma(
   // or two steps, and the other waves of the SIMD cover its load latency.
   for (int e0 = r0 + 32 * w; e0 < r1; e0 += 32 * W) {  // uniform over the wave
     KvStep f;
-    kv_issue(f, irow, e0, r1, vis, col, grp, kb, vb, tok);
-    kv_consume(f, st, qf, vt, wbase, rbase, c_log2);
+    if (kv_issue<SKIP>(f, irow, e0, r1, vis, col, grp, kb, vb, tok))
+      kv_consume(f, st, qf, vt, wbase, rbase, c_log2);
   }
   float l = xgroup_sum(st.l);
   float m = st.m;
@@ -632,7 +642,13 @@ int launch_index_path(const void* q, const void* kc, const void* vc, const int32
   const dim3 block(kWave * gpw * sp.waves_per_head);
   if constexpr (DT == CLSA_BF16) {
 #define CLSA_SPLIT_MFMA(W)                                                                   \
-  hipLaunchKernelGGL((attn_split_mfma<G, W>), grid, block, 0, stream,                        \
+  if (sp.skip_empty_steps)                                                                   \
+    hipLaunchKernelGGL((attn_split_mfma<G, W, true>), grid, block, 0, stream,                \
+                       static_cast<const char*>(q), static_cast<const char*>(kc),            \
+                       static_cast<const char*>(vc), idx, k, out, lse, T, Hkv, kv_len, L_cap, \
+                       c_log2, sp.rows_per_split, partials);                                 \
+  else                                                                                       \
+  hipLaunchKernelGGL((attn_split_mfma<G, W, false>), grid, block, 0, stream,                 \
                      static_cast<const char*>(q), static_cast<const char*>(kc),              \
                      static_cast<const char*>(vc), idx, k, out, lse, T, Hkv, kv_len, L_cap,  \
                      c_log2, sp.rows_per_split, partials)
@@ -702,6 +718,7 @@ AttnSplit attn_split(int B, int T, int Hkv, int k, bool mfma) {
   int rows = (int)((k + s - 1) / s);
   rows = (rows + step * W - 1) / (step * W) * (step * W);
   L.waves_per_head = W;
+  L.skip_empty_steps = false;
   L.rows_per_split = rows;
   L.splits = (k + rows - 1) / rows;
   return L;
@@ -717,8 +734,10 @@ size_t attn_partial_floats(int B, int T, int Hq, int Hkv, int k) {
 
 int launch_sparse_attn(const void* q, const void* kc, const void* vc, int dtype, const int32_t* idx,
                        int k, void* out, float* lse, int B, int T, int Hq, int Hkv, int D,
-                       int kv_len, int L_cap, float scale, float* partials, hipStream_t stream) {
-  const AttnSplit sp = attn_split(B, T, Hkv, k, dtype == CLSA_BF16);
+                       int kv_len, int L_cap, float scale, float* partials, bool skip_empty_steps,
+                       hipStream_t stream) {
+  AttnSplit sp = attn_split(B, T, Hkv, k, dtype == CLSA_BF16);
+  sp.skip_empty_steps = skip_empty_steps;
   const float c_log2 = (scale > 0.f ? scale : 1.f / sqrtf((float)D)) * kLog2e;
   const int G = Hq / Hkv;
   if (dtype == CLSA_BF16)

@@ -25,7 +25,9 @@
 //      the candidates number fewer than k or a chunk overflowed its segment,
 //      it redoes the row on its own (LDS histogram of the full row, ordered
 //      candidate pass), so the result is exact whatever the sample did.
-// Rows whose visible count is <= k take every visible position.
+// Rows whose visible count is <= k take every visible position. With a
+// per-row count k_rows[row] (clamped to [0, k]), a row keeps its k_rows[row]
+// best positions and the rest of its k slots hold -1.
 #include "kernels.h"
 
 namespace clsa {
@@ -295,7 +297,9 @@ __device__ int histogram_and_candidates(const float* srow, int vis, int k, uint3
 __global__ __launch_bounds__(kFilterThreads) void topk_filter(const float* __restrict__ scores,
                                                               uint32_t* __restrict__ counts,
                                                               int2* __restrict__ cand, int T,
-                                                              int kv_len, int k, int nchunks) {
+                                                              int kv_len, int k,
+                                                              const int32_t* __restrict__ k_rows,
+                                                              int nchunks) {
   __shared__ uint32_t h[kBins0];
   __shared__ int tmp[17];
   __shared__ int res[2];
@@ -303,7 +307,8 @@ __global__ __launch_bounds__(kFilterThreads) void topk_filter(const float* __res
   const int vis = kv_len - T + (row % T) + 1;
   const int c0 = blockIdx.x * kChunk;
   uint32_t* cnt = counts + (size_t)row * nchunks + blockIdx.x;
-  if (vis <= k || c0 >= vis) {
+  if (k_rows) k = min(max(k_rows[row], 0), k);
+  if (vis <= k || c0 >= vis || k == 0) {
     if (threadIdx.x == 0) *cnt = 0u;
     return;
   }
@@ -364,7 +369,9 @@ __global__ __launch_bounds__(kThreads) void topk_select(const float* __restrict_
                                                         const int2* __restrict__ cand,
                                                         int32_t* __restrict__ spill,
                                                         int32_t* __restrict__ idx, int T,
-                                                        int kv_len, int k, int nchunks) {
+                                                        int kv_len, int k,
+                                                        const int32_t* __restrict__ k_rows,
+                                                        int nchunks) {
   __shared__ uint32_t h[kBins0 * (1 + kHistCopies)];
   __shared__ int32_t lpos[kLdsCap];
   __shared__ uint32_t lkey[kLdsCap];
@@ -374,7 +381,13 @@ __global__ __launch_bounds__(kThreads) void topk_select(const float* __restrict_
   __shared__ int res[2];
   const int row = blockIdx.x;
   const int vis = kv_len - T + (row % T) + 1;
-  int32_t* out = idx + (size_t)row * k;
+  int32_t* out = idx + (size_t)row * k;  // k slots
+  if (k_rows) {  // this row keeps kr positions; slots kr .. k-1 hold -1
+    const int kr = min(max(k_rows[row], 0), k);
+    for (int i = kr + threadIdx.x; i < k; i += kThreads) out[i] = -1;
+    k = kr;
+    if (k == 0) return;
+  }
   if (vis <= k) {  // every visible position, in order
     for (int i = threadIdx.x; i < k; i += kThreads) out[i] = i < vis ? i : -1;
     return;
@@ -462,19 +475,19 @@ TopkBuffers topk_buffers(int rows, int kv_len) {
   return b;
 }
 
-int launch_topk(const float* scores, int B, int T, int kv_len, int k, int32_t* idx,
-                uint32_t* counts, int32_t* cand, int32_t* spill, hipStream_t stream) {
+int launch_topk(const float* scores, int B, int T, int kv_len, int k, const int32_t* k_rows,
+                int32_t* idx, uint32_t* counts, int32_t* cand, int32_t* spill, hipStream_t stream) {
   const int rows = B * T;
   const TopkBuffers tb = topk_buffers(rows, kv_len);
   if (tb.nchunks > kTopkMaxChunks)
     return set_error(CLSA_ERR_UNSUPPORTED, "topk: kv_len=%d above %d", kv_len, kTopkMaxChunks * kChunk);
   int2* segs = reinterpret_cast<int2*>(cand);
   hipLaunchKernelGGL(topk_filter, dim3(tb.nchunks, rows), dim3(kFilterThreads), 0, stream, scores,
-                     counts, segs, T, kv_len, k, tb.nchunks);
+                     counts, segs, T, kv_len, k, k_rows, tb.nchunks);
   int rc = check_launch("topk_filter");
   if (rc) return rc;
   hipLaunchKernelGGL(topk_select, dim3(rows), dim3(kThreads), 0, stream, scores, counts, segs, spill,
-                     idx, T, kv_len, k, tb.nchunks);
+                     idx, T, kv_len, k, k_rows, tb.nchunks);
   return check_launch("topk_select");
 }
 
