@@ -382,6 +382,13 @@ def main():
         us_paged = per_launch_us(lambda i: clsa.block_paged_attn(X.q[0], X.k_cache[0], X.v_cache[0], indptr,
                                                                  indices, block, kv_len=wl.kv_len, out=out_b,
                                                                  lse=lse_b))
+        # The same comparator over head-major copies of the caches.
+        kh = X.k_cache[0].transpose(1, 2).contiguous()
+        vh = X.v_cache[0].transpose(1, 2).contiguous()
+        us_paged_hm = per_launch_us(lambda i: clsa.block_paged_attn(X.q[0], kh, vh, indptr, indices, block,
+                                                                    kv_len=wl.kv_len, out=out_b, lse=lse_b,
+                                                                    head_major=True))
+        del kh, vh
         pos = min(n_blocks * block, wl.kv_len)
         vis_sum = sum(min(pos, wl.kv_len - wl.T + t + 1) for t in range(wl.T))  # upper bound of keys seen
         flops = 4.0 * wl.B * wl.Hq * wl.D * vis_sum
@@ -390,6 +397,7 @@ def main():
             "union_blocks_per_group": n_blocks,
             "block_union_build_us": us_union,
             "block_paged_attn_us": us_paged,
+            "block_paged_attn_head_major_us": us_paged_hm,
             "block_paged_attn_tflops_upper": flops / (us_paged * 1e-6) / 1e12,
             "sparse_attn_us": us_attn,
         }

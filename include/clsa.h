@@ -255,6 +255,21 @@ int clsa_block_paged_attn(const void* q, const void* k_cache,
                           float scale, void* stream);
 
 /*
+ * clsa_block_paged_attn over head-major caches: k_cache and v_cache are
+ * [B, Hkv, L_cap, D], so every (batch, KV head, block) is one contiguous
+ * piece of memory, the layout CompactAttention's execution step reads in
+ * place (CompactAttention summary, "Méthodologie", execution step:
+ * zero-copy paged attention over the block table). Everything else as
+ * clsa_block_paged_attn.
+ */
+int clsa_block_paged_attn_hm(const void* q, const void* k_cache,
+                             const void* v_cache, int dtype,
+                             const int32_t* kv_indptr,
+                             const int32_t* kv_indices, int block, void* out,
+                             float* lse, int B, int T, int Hq, int Hkv, int D,
+                             int kv_len, int L_cap, float scale, void* stream);
+
+/*
  * Appends T new tokens per batch element to the caches: every extra token of
  * context adds a K and a V row (CLSA article, opening section), written once
  * into the cache that all cross-decoder layers share (CLSA article,

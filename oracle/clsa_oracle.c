@@ -447,12 +447,19 @@ int orc_block_union(const int32_t* idx, int B, int T, int k, int kv_len, int blo
 /*
  * Dense softmax attention of query (b,t,h) over every position s inside the
  * blocks of table (b, g) with s < visible(t) (causal within the chunk).
- * Same arithmetic and output convention as orc_sparse_attn.
+ * Same arithmetic and output convention as orc_sparse_attn. Caches are
+ * token-major [B, L_cap, Hkv, D], or with head_major [B, Hkv, L_cap, D]
+ * ([CA] "Méthodologie": head-major layout read in place).
  */
+static size_t orc_kv_at(int head_major, int b, long s, int g, int d, int Hkv, int L_cap, int D) {
+  return head_major ? (((size_t)b * Hkv + g) * L_cap + s) * D + d
+                    : (((size_t)b * L_cap + s) * Hkv + g) * D + d;
+}
+
 int orc_block_attn(const void* q, const void* kc, const void* vc, int dtype,
                    const int32_t* kv_indptr, const int32_t* kv_indices, int block,
                    double* out, double* lse, int B, int T, int Hq, int Hkv, int D,
-                   int kv_len, int L_cap, double scale) {
+                   int kv_len, int L_cap, double scale, int head_major) {
   if (B < 1 || T < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv || D < 1 || block < 1 ||
       kv_len < T || L_cap < kv_len)
     return -1;
@@ -488,7 +495,7 @@ int orc_block_attn(const void* q, const void* kc, const void* vc, int dtype,
           double dot = 0.0;
           for (int d = 0; d < D; d++)
             dot += orc_elem(q, (((size_t)b * T + t) * Hq + h) * D + d, dtype) *
-                   orc_elem(kc, (((size_t)b * L_cap + sel[j]) * Hkv + g) * D + d, dtype);
+                   orc_elem(kc, orc_kv_at(head_major, b, sel[j], g, d, Hkv, L_cap, D), dtype);
           z[j] = scale * dot;
           if (z[j] > m) m = z[j];
         }
@@ -497,7 +504,7 @@ int orc_block_attn(const void* q, const void* kc, const void* vc, int dtype,
           double p = exp(z[j] - m);
           l += p;
           for (int d = 0; d < D; d++)
-            o[d] += p * orc_elem(vc, (((size_t)b * L_cap + sel[j]) * Hkv + g) * D + d, dtype);
+            o[d] += p * orc_elem(vc, orc_kv_at(head_major, b, sel[j], g, d, Hkv, L_cap, D), dtype);
         }
         for (int d = 0; d < D; d++) o[d] /= l;
         *l_out = m + log(l);

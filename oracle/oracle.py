@@ -52,7 +52,7 @@ def _load():
                 [I, P, P, P, P, I, P, P, P, I, P, P, P] + [I] * 10 + [P, D, P]
             )
             lib.orc_block_union.argtypes = [P, I, I, I, I, I, I, P, P]
-            lib.orc_block_attn.argtypes = [P, P, P, I, P, P, I, P, P] + [I] * 7 + [D]
+            lib.orc_block_attn.argtypes = [P, P, P, I, P, P, I, P, P] + [I] * 7 + [D, I]
             lib.orc_cache_append.argtypes = [P, P, I, I, ctypes.c_long, I, I]
             for f in (
                 lib.orc_decode,
@@ -198,16 +198,22 @@ def block_union(idx, kv_len, block, Hkv):
     return indptr, indices[: indptr[-1]].copy()
 
 
-def block_attn(q, k_cache, v_cache, dtype, kv_indptr, kv_indices, block, kv_len, scale=0.0):
-    """Dense causal attention over a block table. Returns (out, lse) float64."""
+def block_attn(q, k_cache, v_cache, dtype, kv_indptr, kv_indices, block, kv_len, scale=0.0,
+               head_major=False):
+    """Dense causal attention over a block table. Returns (out, lse) float64.
+    Caches [B,L_cap,Hkv,D], or [B,Hkv,L_cap,D] with head_major."""
     q, k_cache, v_cache = (_c(x, _DT[dtype]) for x in (q, k_cache, v_cache))
     kv_indptr, kv_indices = _c(kv_indptr, np.int32), _c(kv_indices, np.int32)
     B, T, Hq, D = q.shape
-    L_cap, Hkv = k_cache.shape[1], k_cache.shape[2]
+    if head_major:
+        Hkv, L_cap = k_cache.shape[1], k_cache.shape[2]
+    else:
+        L_cap, Hkv = k_cache.shape[1], k_cache.shape[2]
     out = np.empty((B, T, Hq, D), np.float64)
     lse = np.empty((B, T, Hq), np.float64)
     rc = _load().orc_block_attn(_p(q), _p(k_cache), _p(v_cache), dtype, _p(kv_indptr), _p(kv_indices),
-                                block, _p(out), _p(lse), B, T, Hq, Hkv, D, kv_len, L_cap, float(scale))
+                                block, _p(out), _p(lse), B, T, Hq, Hkv, D, kv_len, L_cap, float(scale),
+                                1 if head_major else 0)
     _check(rc, "block_attn")
     return out, lse
 

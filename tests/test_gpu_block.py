@@ -64,3 +64,26 @@ def test_block_paged_attention_matches_oracle(B, T, L, k, block, Hq, Hkv):
     ref_o, ref_l = oracle.block_attn(raw(q), raw(kc), raw(vc), inp.BF16, r_ptr, r_ind, block, L)
     assert max_abs(out_f64(out), ref_o) <= TOL_OUT[inp.BF16]
     lse_close(lse.cpu().numpy(), ref_l, TOL_LSE[inp.BF16])
+
+
+@pytest.mark.parametrize("B,T,L,k,block,Hq,Hkv", [
+    (1, 8, 1500, 64, 64, 32, 8),
+    (2, 70, 1000, 20, 16, 16, 16),
+    (1, 9, 2000, 30, 48, 64, 8),
+])
+def test_block_paged_attention_head_major_matches_oracle(B, T, L, k, block, Hq, Hkv):
+    """Head-major caches [B, Hkv, L, D] (CompactAttention summary,
+    "Méthodologie": blocks read in place from the head-major layout)."""
+    announce("block_paged_attn_hm", B, T, L, k, block, Hq, Hkv)
+    D = 128
+    q = inp.randn((B, T, Hq, D), inp.BF16, 91, DEV)
+    kh = inp.randn((B, Hkv, L, D), inp.BF16, 92, DEV)
+    vh = inp.randn((B, Hkv, L, D), inp.BF16, 93, DEV)
+    idx = _index(B, T, L, k, 94)
+    indptr, indices = clsa.block_union_build(idx.to(DEV), L, block, Hkv)
+    out, lse = clsa.block_paged_attn(q, kh, vh, indptr, indices, block, kv_len=L, head_major=True)
+    torch.cuda.synchronize()
+    r_ptr, r_ind = oracle.block_union(idx.numpy(), L, block, Hkv)
+    ref_o, ref_l = oracle.block_attn(raw(q), raw(kh), raw(vh), inp.BF16, r_ptr, r_ind, block, L, head_major=True)
+    assert max_abs(out_f64(out), ref_o) <= TOL_OUT[inp.BF16]
+    lse_close(lse.cpu().numpy(), ref_l, TOL_LSE[inp.BF16])

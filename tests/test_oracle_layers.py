@@ -161,3 +161,24 @@ def test_full_union_equals_dense_causal_attention():
     mask = torch.arange(L)[None, :] < (L - T + torch.arange(T) + 1)[:, None]
     ref = F.scaled_dot_product_attention(qt, kt, vt, attn_mask=mask).permute(0, 2, 1, 3).numpy()
     np.testing.assert_allclose(out, ref, rtol=1e-12, atol=1e-12)
+
+
+def test_block_attention_head_major_layout_gives_the_same_result():
+    """CompactAttention summary, "Méthodologie": the execution step reads the
+    blocks in place from a head-major cache. The layout changes addresses
+    only, so the oracle's result is bit-identical on the permuted cache."""
+    rng = np.random.default_rng(77)
+    B, T, L, Hq, Hkv, D, k, block = 2, 6, 90, 4, 2, 8, 10, 16
+    q = _f32(rng.standard_normal((B, T, Hq, D)))
+    K = _f32(rng.standard_normal((B, L, Hkv, D)))
+    V = _f32(rng.standard_normal((B, L, Hkv, D)))
+    idx = oracle.topk(rng.standard_normal((B, T, L)), k)
+    ptr, ind = oracle.block_union(idx, L, block, Hkv)
+    o1, l1 = oracle.block_attn(q, K, V, oracle.F32, ptr, ind, block, L)
+    Kh, Vh = (np.ascontiguousarray(x.transpose(0, 2, 1, 3)) for x in (K, V))
+    o2, l2 = oracle.block_attn(q, Kh, Vh, oracle.F32, ptr, ind, block, L, head_major=True)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+    # And a head-major cache read as if token-major gives a different answer.
+    o3, _ = oracle.block_attn(q, np.ascontiguousarray(Kh.reshape(K.shape)),
+                              np.ascontiguousarray(Vh.reshape(V.shape)), oracle.F32, ptr, ind, block, L)
+    assert not np.allclose(o1, o3)

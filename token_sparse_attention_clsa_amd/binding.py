@@ -84,6 +84,7 @@ def load() -> ctypes.CDLL:
         "clsa_decode_step": (I, [ctypes.POINTER(StepDesc), P, SZ, P]),
         "clsa_block_union_build": (I, [P] + [I] * 6 + [P, P, P, SZ, P]),
         "clsa_block_paged_attn": (I, [P, P, P, I, P, P, I, P, P] + [I] * 7 + [F, P]),
+        "clsa_block_paged_attn_hm": (I, [P, P, P, I, P, P, I, P, P] + [I] * 7 + [F, P]),
         "clsa_cache_append": (I, [P, P, P, P, I, P, P] + [I] * 8 + [P]),
     }
     for name, (res, args) in sig.items():
@@ -311,13 +312,19 @@ def block_union_build(idx: torch.Tensor, kv_len: int, block: int, Hkv: int):
 
 
 def block_paged_attn(q, k_cache, v_cache, kv_indptr, kv_indices, block: int, kv_len: Optional[int] = None,
-                     scale: float = 0.0, out=None, lse=None, want_lse: bool = True):
-    """clsa_block_paged_attn. Returns (out, lse)."""
+                     scale: float = 0.0, out=None, lse=None, want_lse: bool = True, head_major: bool = False):
+    """clsa_block_paged_attn (token-major caches [B,L_cap,Hkv,D]) or, with
+    head_major, clsa_block_paged_attn_hm (caches [B,Hkv,L_cap,D]). Returns (out, lse)."""
     _dev(q, "q", (torch.bfloat16,))
     B, T, Hq, D = q.shape
-    L_cap, Hkv = k_cache.shape[1], k_cache.shape[2]
-    _dev(k_cache, "k_cache", (q.dtype,), (B, L_cap, Hkv, D))
-    _dev(v_cache, "v_cache", (q.dtype,), (B, L_cap, Hkv, D))
+    if head_major:
+        Hkv, L_cap = k_cache.shape[1], k_cache.shape[2]
+        shape = (B, Hkv, L_cap, D)
+    else:
+        L_cap, Hkv = k_cache.shape[1], k_cache.shape[2]
+        shape = (B, L_cap, Hkv, D)
+    _dev(k_cache, "k_cache", (q.dtype,), shape)
+    _dev(v_cache, "v_cache", (q.dtype,), shape)
     _dev(kv_indptr, "kv_indptr", (torch.int32,), (B * Hkv + 1,))
     _dev(kv_indices, "kv_indices", (torch.int32,))
     kv_len = L_cap if kv_len is None else kv_len
@@ -325,10 +332,10 @@ def block_paged_attn(q, k_cache, v_cache, kv_indptr, kv_indices, block: int, kv_
         out = torch.empty_like(q)
     if lse is None and want_lse:
         lse = torch.empty((B, T, Hq), dtype=torch.float32, device=q.device)
-    rc = load().clsa_block_paged_attn(_ptr(q), _ptr(k_cache), _ptr(v_cache), _DT[q.dtype],
-                                      _ptr(kv_indptr), _ptr(kv_indices), block, _ptr(out), _ptr(lse),
-                                      B, T, Hq, Hkv, D, kv_len, L_cap, float(scale), _stream())
-    _check(rc, "clsa_block_paged_attn")
+    fn = load().clsa_block_paged_attn_hm if head_major else load().clsa_block_paged_attn
+    rc = fn(_ptr(q), _ptr(k_cache), _ptr(v_cache), _DT[q.dtype], _ptr(kv_indptr), _ptr(kv_indices), block,
+            _ptr(out), _ptr(lse), B, T, Hq, Hkv, D, kv_len, L_cap, float(scale), _stream())
+    _check(rc, "clsa_block_paged_attn_hm" if head_major else "clsa_block_paged_attn")
     return out, lse
 
 

@@ -346,10 +346,10 @@ int clsa_block_union_build(const int32_t* idx, int B, int T, int k, int kv_len, 
                             static_cast<hipStream_t>(stream));
 }
 
-int clsa_block_paged_attn(const void* q, const void* k_cache, const void* v_cache, int dtype,
+static int block_paged_attn(const void* q, const void* k_cache, const void* v_cache, int dtype,
                           const int32_t* kv_indptr, const int32_t* kv_indices, int block, void* out,
                           float* lse, int B, int T, int Hq, int Hkv, int D, int kv_len, int L_cap,
-                          float scale, void* stream) {
+                          float scale, bool head_major, void* stream) {
   if (!q || !k_cache || !v_cache || !kv_indptr || !kv_indices || !out)
     return set_error(CLSA_ERR_INVALID_ARG, "block_paged_attn: null pointer");
   int rc = check_shape(B, T, kv_len, L_cap);
@@ -366,8 +366,24 @@ int clsa_block_paged_attn(const void* q, const void* k_cache, const void* v_cach
   if (!(scale == scale) || isinf(scale))
     return set_error(CLSA_ERR_INVALID_ARG, "block_paged_attn: scale must be finite");
   return launch_block_paged_attn(q, k_cache, v_cache, dtype, kv_indptr, kv_indices, block, out, lse,
-                                 B, T, Hq, Hkv, D, kv_len, L_cap, scale,
+                                 B, T, Hq, Hkv, D, kv_len, L_cap, scale, head_major,
                                  static_cast<hipStream_t>(stream));
+}
+
+int clsa_block_paged_attn(const void* q, const void* k_cache, const void* v_cache, int dtype,
+                          const int32_t* kv_indptr, const int32_t* kv_indices, int block, void* out,
+                          float* lse, int B, int T, int Hq, int Hkv, int D, int kv_len, int L_cap,
+                          float scale, void* stream) {
+  return block_paged_attn(q, k_cache, v_cache, dtype, kv_indptr, kv_indices, block, out, lse, B, T, Hq,
+                          Hkv, D, kv_len, L_cap, scale, false, stream);
+}
+
+int clsa_block_paged_attn_hm(const void* q, const void* k_cache, const void* v_cache, int dtype,
+                             const int32_t* kv_indptr, const int32_t* kv_indices, int block,
+                             void* out, float* lse, int B, int T, int Hq, int Hkv, int D, int kv_len,
+                             int L_cap, float scale, void* stream) {
+  return block_paged_attn(q, k_cache, v_cache, dtype, kv_indptr, kv_indices, block, out, lse, B, T, Hq,
+                          Hkv, D, kv_len, L_cap, scale, true, stream);
 }
 
 int clsa_cache_append(const void* k_new, const void* v_new, void* k_cache, void* v_cache, int dtype,

@@ -51,7 +51,7 @@ __global__ __launch_bounds__(kWaves * kWave) void block_attn_mfma(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc,
     const int32_t* __restrict__ kv_indptr, const int32_t* __restrict__ kv_indices, int block,
     uint16_t* __restrict__ out, float* __restrict__ lse, int T, int Hkv, int kv_len, int L_cap,
-    float c_log2) {
+    float c_log2, int head_major) {
   constexpr int QPW = 16 / G;            // queries per wave
   __shared__ __attribute__((aligned(16))) uint8_t kt[kKT * kKPitch];
   __shared__ __attribute__((aligned(16))) uint8_t vt[kD * kVPitch];
@@ -86,9 +86,13 @@ __global__ __launch_bounds__(kWaves * kWave) void block_attn_mfma(
   const int tab = b * Hkv + g;
   const int32_t* list = kv_indices + kv_indptr[tab];
   const int npos = (kv_indptr[tab + 1] - kv_indptr[tab]) * block;
-  const uint16_t* kbase = kc + ((size_t)b * L_cap * Hkv + g) * kD;
-  const uint16_t* vbase = vc + ((size_t)b * L_cap * Hkv + g) * kD;
-  const size_t tok = (size_t)Hkv * kD;
+  // Token-major [B, L_cap, Hkv, D]: a token's rows of the Hkv heads are
+  // adjacent. Head-major [B, Hkv, L_cap, D]: each (b, g) is one contiguous
+  // [L_cap, D] slab, so a block of positions is one contiguous piece.
+  const size_t head0 = head_major ? ((size_t)b * Hkv + g) * L_cap * kD : ((size_t)b * L_cap * Hkv + g) * kD;
+  const uint16_t* kbase = kc + head0;
+  const uint16_t* vbase = vc + head0;
+  const size_t tok = head_major ? (size_t)kD : (size_t)Hkv * kD;
 
   // Staging: 64 rows x 16 chunks of 16 bytes for K and for V; thread c moves
   // chunks c and c + 512 of each (row = chunk / 16, d0 = 8 * (chunk % 16)).
@@ -232,12 +236,12 @@ __global__ __launch_bounds__(kWaves * kWave) void block_attn_mfma(
 template <int G>
 int launch_g(const void* q, const void* kc, const void* vc, const int32_t* indptr,
              const int32_t* indices, int block, void* out, float* lse, int B, int T, int Hkv,
-             int kv_len, int L_cap, float c_log2, hipStream_t stream) {
+             int kv_len, int L_cap, float c_log2, bool head_major, hipStream_t stream) {
   dim3 grid((T + kRows / G - 1) / (kRows / G), Hkv, B);
   hipLaunchKernelGGL((block_attn_mfma<G>), grid, dim3(kWaves * kWave), 0, stream,
                      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(kc),
                      static_cast<const uint16_t*>(vc), indptr, indices, block,
-                     static_cast<uint16_t*>(out), lse, T, Hkv, kv_len, L_cap, c_log2);
+                     static_cast<uint16_t*>(out), lse, T, Hkv, kv_len, L_cap, c_log2, head_major ? 1 : 0);
   return check_launch("block_attn_mfma");
 }
 
@@ -246,13 +250,13 @@ int launch_g(const void* q, const void* kc, const void* vc, const int32_t* indpt
 int launch_block_attn_mfma(const void* q, const void* kc, const void* vc,
                            const int32_t* kv_indptr, const int32_t* kv_indices, int block,
                            void* out, float* lse, int B, int T, int Hq, int Hkv, int D, int kv_len,
-                           int L_cap, float scale, hipStream_t stream) {
+                           int L_cap, float scale, bool head_major, hipStream_t stream) {
   const float c_log2 = (scale > 0.f ? scale : 1.f / sqrtf((float)D)) * kLog2e;
   switch (Hq / Hkv) {
-    case 1: return launch_g<1>(q, kc, vc, kv_indptr, kv_indices, block, out, lse, B, T, Hkv, kv_len, L_cap, c_log2, stream);
-    case 2: return launch_g<2>(q, kc, vc, kv_indptr, kv_indices, block, out, lse, B, T, Hkv, kv_len, L_cap, c_log2, stream);
-    case 4: return launch_g<4>(q, kc, vc, kv_indptr, kv_indices, block, out, lse, B, T, Hkv, kv_len, L_cap, c_log2, stream);
-    case 8: return launch_g<8>(q, kc, vc, kv_indptr, kv_indices, block, out, lse, B, T, Hkv, kv_len, L_cap, c_log2, stream);
+    case 1: return launch_g<1>(q, kc, vc, kv_indptr, kv_indices, block, out, lse, B, T, Hkv, kv_len, L_cap, c_log2, head_major, stream);
+    case 2: return launch_g<2>(q, kc, vc, kv_indptr, kv_indices, block, out, lse, B, T, Hkv, kv_len, L_cap, c_log2, head_major, stream);
+    case 4: return launch_g<4>(q, kc, vc, kv_indptr, kv_indices, block, out, lse, B, T, Hkv, kv_len, L_cap, c_log2, head_major, stream);
+    case 8: return launch_g<8>(q, kc, vc, kv_indptr, kv_indices, block, out, lse, B, T, Hkv, kv_len, L_cap, c_log2, head_major, stream);
   }
   return set_error(CLSA_ERR_UNSUPPORTED, "block_paged_attn: Hq/Hkv=%d", Hq / Hkv);
 }

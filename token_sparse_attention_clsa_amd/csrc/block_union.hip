@@ -19,7 +19,7 @@ namespace clsa {
 int launch_block_attn_mfma(const void* q, const void* kc, const void* vc,
                            const int32_t* kv_indptr, const int32_t* kv_indices, int block,
                            void* out, float* lse, int B, int T, int Hq, int Hkv, int D, int kv_len,
-                           int L_cap, float scale, hipStream_t stream);
+                           int L_cap, float scale, bool head_major, hipStream_t stream);
 
 namespace {
 
@@ -101,10 +101,11 @@ bool block_paged_attn_supported(int dtype, int Hq, int Hkv, int D, int block) {
 int launch_block_paged_attn(const void* q, const void* kc, const void* vc, int dtype,
                             const int32_t* kv_indptr, const int32_t* kv_indices, int block,
                             void* out, float* lse, int B, int T, int Hq, int Hkv, int D,
-                            int kv_len, int L_cap, float scale, hipStream_t stream) {
+                            int kv_len, int L_cap, float scale, bool head_major,
+                            hipStream_t stream) {
   (void)dtype;  // bf16 only (checked by the caller)
   return launch_block_attn_mfma(q, kc, vc, kv_indptr, kv_indices, block, out, lse, B, T, Hq, Hkv, D,
-                                kv_len, L_cap, scale, stream);
+                                kv_len, L_cap, scale, head_major, stream);
 }
 
 }  // namespace clsa

@@ -63,10 +63,12 @@ int launch_sparse_attn(const void* q, const void* kc, const void* vc, int dtype,
 size_t block_union_ws_bytes(int B, int kv_len, int block);
 int launch_block_union(const int32_t* idx, int B, int T, int k, int kv_len, int block, int Hkv,
                        int32_t* kv_indptr, int32_t* kv_indices, void* ws, hipStream_t stream);
+// head_major: caches are [B, Hkv, L_cap, D] instead of [B, L_cap, Hkv, D].
 int launch_block_paged_attn(const void* q, const void* kc, const void* vc, int dtype,
                             const int32_t* kv_indptr, const int32_t* kv_indices, int block,
                             void* out, float* lse, int B, int T, int Hq, int Hkv, int D,
-                            int kv_len, int L_cap, float scale, hipStream_t stream);
+                            int kv_len, int L_cap, float scale, bool head_major,
+                            hipStream_t stream);
 bool block_paged_attn_supported(int dtype, int Hq, int Hkv, int D, int block);
 
 }  // namespace clsa
