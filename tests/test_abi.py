@@ -170,3 +170,29 @@ def test_cache_append_rejects(lib):
     assert call(k_new=A + 4) == -1 and b"misaligned" in lib.clsa_last_error()
     assert call(k_new=C + 4096) == -1 and b"overlap" in lib.clsa_last_error()  # source inside a cache
     assert call(B=0) == -1
+
+
+def test_topk_vark_and_head_major_reject(lib):
+    assert lib.clsa_topk_vark(FAKE, 1, 1, 100, 5, FAKE + 2, FAKE, FAKE, 1 << 20, None) == -1   # misaligned counts
+    assert lib.clsa_topk_vark(FAKE, 1, 1, 100, 0, FAKE, FAKE, FAKE, 1 << 20, None) == -1       # k = 0
+    assert lib.clsa_topk_vark(FAKE, 1, 1, 100, 5, FAKE, FAKE, None, 0, None) == -3            # no workspace
+    assert lib.clsa_block_paged_attn_hm(FAKE, FAKE, FAKE, 0, FAKE, FAKE, 64, FAKE, None, 1, 1, 32, 8,
+                                        128, 100, 100, 0.0, None) == -2   # f32 comparator not built
+    assert lib.clsa_block_paged_attn_hm(None, FAKE, FAKE, 1, FAKE, FAKE, 64, FAKE, None, 1, 1, 32, 8,
+                                        128, 100, 100, 0.0, None) == -1
+
+
+def test_step_descriptor_layout_matches_header(lib):
+    """The binding's descriptor mirrors clsa_step_desc field for field: a
+    misaligned per-query count pointer set through it is seen (and rejected)
+    by the library."""
+    import ctypes
+    from token_sparse_attention_clsa_amd import binding
+    n = 1
+    P = ctypes.c_void_p
+    arr = (P * n)(FAKE)
+    src = (ctypes.c_int32 * n)(0)
+    d = binding.StepDesc(n, src, arr, arr, arr, arr, ctypes.POINTER(P)(), arr, arr, arr, FAKE, 1, 1,
+                         1, 1, 32, 8, 128, 64, 128, 100, 100, 16, 0.0, ctypes.POINTER(P)(), FAKE + 2)
+    assert lib.clsa_decode_step(ctypes.byref(d), FAKE, 1 << 30, None) == -1
+    assert b"k_per_query" in lib.clsa_last_error()
