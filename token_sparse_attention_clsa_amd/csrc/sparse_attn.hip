@@ -261,9 +261,10 @@ __global__ __launch_bounds__(kWave * kMaxWaves) void attn_split_kernel(
   }
 }
 
-// bf16 split kernel on matrix cores (same grid, work split and outputs as
-// attn_split_kernel). One wave per KV head g; entries go in steps of 32,
-// as two tiles of 16 keys. Lane l = 16 * grp + col.
+// bf16 split kernel on matrix cores (same outputs as attn_split_kernel).
+// W waves (1, 2 or 4; see attn_split) per (query, split, KV head g); each
+// wave takes 32-entry steps, as two tiles of 16 keys, reading the positions
+// it needs straight from the query's index row. Lane l = 16 * grp + col.
 //  - Scores: S^T[key, h] = K[key, :] . q[h, :] with v_mfma_f32_16x16x32_bf16.
 //    A = 16 gathered K rows (lane: key col, d = 8 * grp + 32 * ks + 0..7),
 //    B = the G query heads (lane: head col, zero for col >= G). Lane
