@@ -104,8 +104,10 @@ TOPK_CASES = [
     ("gauss", 1, 6, 5000, 4997),       # causal rows: 2 with fewer than k visible, 1 with exactly k
     ("ties", 1, 64, 8192, 512),        # many causal rows
     ("gauss", 1, 1, 4097, 4096),
-    ("strided", 1, 1, 131072, 3000),   # a strided sample sees only the high positions: full-row redo
+    ("strided", 1, 1, 131072, 3000),   # 2048 tied high positions, then Gaussian ones
     ("strided", 2, 1, 131072, 1000),
+    ("sampled", 1, 1, 131072, 3000),   # the filter's sample sees only the high positions: full-row redo
+    ("sampled", 1, 1, 50001, 1000),
     ("needle", 2, 1, 131073, 2048),    # misaligned second row
     ("desc", 1, 1, 40000, 2048),       # the top k fill one 4096-chunk: its candidate segment overflows
 ]

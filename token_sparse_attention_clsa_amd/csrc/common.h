@@ -47,14 +47,18 @@ __device__ __forceinline__ uint32_t score_key(float f) {
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 
-template <typename T>
-__device__ __forceinline__ T wave_inclusive_scan(T v) {
-  const int lane = lane_id();
-#pragma unroll
-  for (int off = 1; off < kWave; off <<= 1) {
-    T n = __shfl_up(v, off, kWave);
-    if (lane >= off) v += n;
-  }
+// Inclusive scan of an int over the 64 lanes of a wave with DPP moves: row_shr
+// 1, 2, 4, 8 scan each row of 16 lanes (a lane whose source lies outside its
+// row adds 0), then row_bcast 15 adds row 0's total into row 1 and row 2's
+// into row 3, and row_bcast 31 adds lane 31's running total into rows 2
+// and 3 (rows outside the row mask keep their value).
+__device__ __forceinline__ int wave_inclusive_scan(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false);  // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false);  // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false);  // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false);  // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);  // row_bcast:15
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);  // row_bcast:31
   return v;
 }
 
@@ -66,27 +70,24 @@ __device__ __forceinline__ T wave_sum(T v) {
 }
 
 // Exclusive scan of one int per thread over the whole block (blockDim.x a
-// multiple of 64, at most 1024). `tmp` is __shared__ int[16 + 1]. Returns the
-// thread's exclusive prefix; *total receives the block total. Contains
-// barriers: every thread of the block must call it.
+// multiple of 64, at most 1024). `tmp` is __shared__ int[16 + 1] (the first
+// blockDim.x / 64 entries are used). Returns the thread's exclusive prefix;
+// *total receives the block total. Contains barriers: every thread of the
+// block must call it, with the whole wave active.
 __device__ __forceinline__ int block_exclusive_scan(int v, int* tmp, int* total) {
   const int lane = lane_id();
-  const int wid = threadIdx.x / kWave;
+  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int nw = blockDim.x / kWave;
-  int inc = wave_inclusive_scan(v);
+  const int inc = wave_inclusive_scan(v);
   if (lane == kWave - 1) tmp[wid] = inc;
   __syncthreads();
-  if (wid == 0) {
-    int x = lane < nw ? tmp[lane] : 0;
-    int xi = wave_inclusive_scan(x);
-    if (lane < nw) tmp[lane] = xi - x;
-    if (lane == nw - 1) tmp[16] = xi;
-  }
-  __syncthreads();
-  int res = tmp[wid] + inc - v;
-  *total = tmp[16];
-  __syncthreads();
-  return res;
+  // Every wave scans the wave totals itself, so no second publishing step.
+  const int x = lane < nw ? tmp[lane] : 0;
+  const int xi = wave_inclusive_scan(x);
+  const int before = __builtin_amdgcn_readlane(xi - x, wid);
+  *total = __builtin_amdgcn_readlane(xi, nw - 1);
+  __syncthreads();  // the totals are read before tmp can be rewritten
+  return before + inc - v;
 }
 
 // ---------------------------------------------------------------------------

@@ -6,22 +6,24 @@
 // padding when fewer than k positions are visible.
 //
 // Scores become order-preserving 32-bit keys (-0 folded onto +0); selection
-// is radix selection on three digits (bits 31..20, 19..8, 7..0). Two
-// launches:
+// is radix selection on digits of at most 12 bits. Two launches:
 //   1. topk_filter (chunks x rows, 256 threads): every workgroup of a row
-//      takes the same deterministic strided sample of the row, histograms the
-//      sample's top digits in LDS and picks the bin where the sample's count
-//      from the top reaches about twice the rank k would have in the sample.
-//      It then writes, in position order, the (position, key) pairs of its
-//      4096-element chunk whose top digit is at or above that bin (at most
-//      kTopkSegCap of them) and their count. With a 2048-element sample the
-//      chance that this keeps fewer than k positions, or more than the cap in
-//      a chunk, is negligible for any smooth score distribution, and the next
-//      kernel checks both anyway.
+//      takes the same deterministic sample of the row (128 runs of 16
+//      consecutive elements, evenly spaced, so the sample costs 128 cache
+//      lines rather than 2048), histograms the sample's top digits in LDS
+//      and picks the bin where the sample's count from the top reaches about
+//      twice the rank k would have in the sample. It then writes, in
+//      position order, the (position, key) pairs of its 4096-element chunk
+//      whose top digit is at or above that bin (at most kTopkSegCap of them)
+//      and their count. With a 2048-element sample the chance that this
+//      keeps fewer than k positions, or more than the cap in a chunk, is
+//      negligible for any smooth score distribution, and the next kernel
+//      checks both anyway.
 //   2. topk_select (rows, 1024 threads): gathers the candidate segments (in
 //      chunk order, hence position order) into LDS and resolves the k-th key
-//      theta exactly with three LDS histograms, then emits, in one ordered
-//      scan, keys above theta and the first `quota` keys equal to theta. If
+//      theta exactly with LDS histograms over the candidates' own key range
+//      (key - min, 12 bits per pass), then emits, in one ordered scan, keys
+//      above theta and the first `quota` keys equal to theta. If
 //      the candidates number fewer than k or a chunk overflowed its segment,
 //      it redoes the row on its own (LDS histogram of the full row, ordered
 //      candidate pass), so the result is exact whatever the sample did.
@@ -38,22 +40,33 @@ constexpr int kThreads = 1024;     // topk_select
 constexpr int kWaves = kThreads / kWave;
 constexpr int kFilterThreads = 256;
 constexpr int kChunk = kTopkChunk; // topk_filter: 16 consecutive elements per thread
-constexpr int kSample = 2048;      // strided sample for the threshold estimate
+constexpr int kSample = 2048;      // sample for the threshold estimate
+constexpr int kSampleRun = 16;     // ... taken as kSample / kSampleRun evenly spaced runs
 constexpr int kTile = 16384;       // fallback tile: 16 waves x 1024 consecutive elements
 constexpr int kLdsCap = 12288;     // candidates kept in LDS
 constexpr int kHistCopies = 2;     // fallback histogram copies
 
 // Finds the bin b (scanning bins from high to low) where the running count
-// first reaches `need`; res[0] = b, res[1] = count in bins above b.
-// Every thread of the block must call it; need must be in [1, total].
+// first reaches `need`; res[0] = b, res[1] = count in bins above b. Thread t
+// takes the `per` consecutive bins below nbins - per * t (consecutive
+// threads, consecutive bins: no LDS bank conflicts); a wave scan, the wave
+// totals through tmp and one barrier give each thread the count above its
+// bins, and the thread where `need` falls walks them. Every thread of the
+// block must call it; need must be in [1, total]; tmp is int[16].
 __device__ void find_bin(const uint32_t* h, int nbins, int need, int* res, int* tmp) {
   const int per = (nbins + blockDim.x - 1) / blockDim.x;
   const int hi = nbins - 1 - (int)threadIdx.x * per;
   int sum = 0;
   for (int j = 0; j < per; j++)
     if (hi - j >= 0) sum += h[hi - j];
-  int total;
-  const int before = block_exclusive_scan(sum, tmp, &total);
+  const int lane = threadIdx.x % kWave;
+  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int nw = blockDim.x / kWave;
+  const int inc = wave_inclusive_scan(sum);
+  if (lane == kWave - 1) tmp[wid] = inc;
+  __syncthreads();
+  const int x = lane < nw ? tmp[lane] : 0;
+  const int before = __builtin_amdgcn_readlane(wave_inclusive_scan(x) - x, wid) + inc - sum;
   if (before < need && need <= before + sum) {
     int acc = before;
     for (int j = 0; j < per && hi - j >= 0; j++) {
@@ -67,6 +80,25 @@ __device__ void find_bin(const uint32_t* h, int nbins, int need, int* res, int* 
     }
   }
   __syncthreads();
+}
+
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+  v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(-1, (int)v, 0x111, 0xf, 0xf, false));
+  v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(-1, (int)v, 0x112, 0xf, 0xf, false));
+  v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(-1, (int)v, 0x114, 0xf, 0xf, false));
+  v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(-1, (int)v, 0x118, 0xf, 0xf, false));
+  v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(-1, (int)v, 0x142, 0xa, 0xf, false));
+  v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(-1, (int)v, 0x143, 0xc, 0xf, false));
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, kWave - 1);
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xf, 0xf, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xf, 0xf, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xf, 0xf, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xf, 0xf, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xa, 0xf, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xc, 0xf, false));
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, kWave - 1);
 }
 
 __global__ __launch_bounds__(256) void fill_zero(uint32_t* p, size_t n) {
@@ -104,33 +136,32 @@ struct SegCand {
   __device__ uint32_t k(int i) const { return (uint32_t)e(i).y; }
 };
 
-// Resolves theta among the candidates and emits the row's selection.
+// Resolves theta, the need-th largest key among the candidates, all of
+// which in play lie in [lo, lo + R) (R a power of two <= 2^32), by radix
+// passes of at most 12 bits on key - lo, then emits the row's selection.
 template <class Acc>
-__device__ void select_and_emit(const Acc& acc, int n, int need0, uint32_t b0, uint32_t* h,
-                                int* res, int* tmp, int32_t* out, int k) {
-  // Digit 1 (bits 19..8) among candidates whose top digit is b0.
-  for (int i = threadIdx.x; i < kBins0; i += blockDim.x) h[i] = 0u;
-  __syncthreads();
-  for (int i = threadIdx.x; i < n; i += blockDim.x) {
-    const uint32_t key = acc.k(i);
-    if ((key >> 20) == b0) atomicAdd(&h[(key >> 8) & 0xfffu], 1u);
+__device__ void select_and_emit(const Acc& acc, int n, int need, uint32_t lo, uint64_t R,
+                                uint32_t* h, int* res, int* tmp, int32_t* out, int k) {
+  while (R > 1) {  // uniform over the workgroup
+    const int bits = 63 - __clzll(R);
+    const int s = bits > 12 ? bits - 12 : 0;
+    const int nb = (int)(R >> s);
+    for (int i = threadIdx.x; i < nb; i += blockDim.x) h[i] = 0u;
+    __syncthreads();
+    for (int i = threadIdx.x; i < n; i += blockDim.x) {
+      const uint32_t key = acc.k(i);
+      if (key >= lo && (uint64_t)(key - lo) < R) atomicAdd(&h[(key - lo) >> s], 1u);
+    }
+    __syncthreads();
+    find_bin(h, nb, need, res, tmp);
+    // Every thread reads res here, before the next pass's first barrier;
+    // it is rewritten only after that pass's third one.
+    lo += (uint32_t)res[0] << s;
+    need -= res[1];
+    R = 1ull << s;
   }
-  __syncthreads();
-  find_bin(h, kBins0, need0, res, tmp);
-  const uint32_t b1 = (uint32_t)res[0];
-  const int need1 = need0 - res[1];
-  const uint32_t pre = (b0 << 12) | b1;
-  // Digit 2 (bits 7..0) among candidates matching the top 24 bits.
-  for (int i = threadIdx.x; i < 256; i += blockDim.x) h[i] = 0u;
-  __syncthreads();
-  for (int i = threadIdx.x; i < n; i += blockDim.x) {
-    const uint32_t key = acc.k(i);
-    if ((key >> 8) == pre) atomicAdd(&h[key & 0xffu], 1u);
-  }
-  __syncthreads();
-  find_bin(h, 256, need1, res, tmp);
-  const uint32_t theta = (pre << 8) | (uint32_t)res[0];
-  const int quota = need1 - res[1];  // how many keys equal to theta are taken
+  const uint32_t theta = lo;
+  const int quota = need;  // how many keys equal to theta are taken
   // Ordered emission: thread t owns the run [t0 + t * run, t0 + (t + 1) * run)
   // of the tile (run <= 16), so up to 16 * blockDim.x candidates take one
   // block scan and no barrier waits behind the output stores.
@@ -168,19 +199,35 @@ __device__ void select_and_emit(const Acc& acc, int n, int need0, uint32_t b0, u
   }
 }
 
-// Full three-level selection of the k largest among n candidates.
+// Selection of the k largest among n >= k candidates. The radix passes run
+// on key - min over the candidates' own key range, so the first pass spreads
+// them over its bins even when they share the top bits of their keys, and a
+// range of at most 2^24 keys takes two passes.
 template <class Acc>
 __device__ void select_top(const Acc& acc, int n, int k, uint32_t* h, int* res, int* tmp,
                            int32_t* out) {
-  for (int i = threadIdx.x; i < kBins0; i += blockDim.x) h[i] = 0u;
+  __shared__ uint32_t mm[2][kWaves];
+  uint32_t mn = 0xffffffffu, mx = 0u;
+  for (int i = threadIdx.x; i < n; i += blockDim.x) {
+    const uint32_t key = acc.k(i);
+    mn = min(mn, key);
+    mx = max(mx, key);
+  }
+  mn = wave_min_u32(mn);
+  mx = wave_max_u32(mx);
+  const int wave = threadIdx.x / kWave, nw = blockDim.x / kWave;
+  if (threadIdx.x % kWave == 0) {
+    mm[0][wave] = mn;
+    mm[1][wave] = mx;
+  }
   __syncthreads();
-  for (int i = threadIdx.x; i < n; i += blockDim.x) atomicAdd(&h[acc.k(i) >> 20], 1u);
-  __syncthreads();
-  find_bin(h, kBins0, k, res, tmp);
-  const uint32_t b0 = (uint32_t)res[0];
-  const int need0 = k - res[1];
-  __syncthreads();  // everyone has read res before select_and_emit reuses it
-  select_and_emit(acc, n, need0, b0, h, res, tmp, out, k);
+  for (int w = 0; w < nw; w++) {
+    mn = min(mn, mm[0][w]);
+    mx = max(mx, mm[1][w]);
+  }
+  const uint64_t span = (uint64_t)(mx - mn) + 1;  // n >= k >= 1, so mx >= mn
+  const uint64_t R = span == 1 ? 1 : 1ull << (64 - __clzll(span - 1));
+  select_and_emit(acc, n, k, mn, R, h, res, tmp, out, k);
 }
 
 template <bool VEC>
@@ -300,7 +347,7 @@ __global__ __launch_bounds__(kFilterThreads) void topk_filter(const float* __res
                                                               int kv_len, int k,
                                                               const int32_t* __restrict__ k_rows,
                                                               int nchunks) {
-  __shared__ uint32_t h[kBins0];
+  __shared__ __attribute__((aligned(16))) uint32_t h[kBins0];
   __shared__ int tmp[17];
   __shared__ int res[2];
   const int row = blockIdx.y;
@@ -313,42 +360,46 @@ __global__ __launch_bounds__(kFilterThreads) void topk_filter(const float* __res
     return;
   }
   const float* srow = scores + (size_t)row * kv_len;
-  // Threshold bin from the row's strided sample (identical in every workgroup).
-  for (int i = threadIdx.x; i < kBins0; i += blockDim.x) h[i] = 0u;
-  __syncthreads();
-  const int m = min(kSample, vis);
-  for (int i = threadIdx.x; i < m; i += blockDim.x)
-    atomicAdd(&h[score_key(srow[(int)((long)i * vis / m)]) >> 20], 1u);
-  __syncthreads();
-  const long expect = ((long)k * m + vis - 1) / vis;  // rank of the k-th key in the sample
-  const int r = (int)min((long)m, 2 * expect + 8);
-  find_bin(h, kBins0, r, res, tmp);
-  const uint32_t b0 = (uint32_t)res[0];
-  // Ordered compaction of this chunk's positions whose top digit is >= b0.
+  // This thread's 16 chunk elements are loaded first, so that their memory
+  // latency overlaps the sample's.
   const int e0 = c0 + threadIdx.x * 16;
-  uint32_t flags = 0;
-  int c = 0;
   uint32_t key[16];
   if (e0 + 15 < vis && (reinterpret_cast<uintptr_t>(srow + e0) & 15) == 0) {
     const float4* p4 = reinterpret_cast<const float4*>(srow + e0);
     float4 v[4] = {p4[0], p4[1], p4[2], p4[3]};
     const float* x = reinterpret_cast<const float*>(v);
 #pragma unroll
-    for (int j = 0; j < 16; j++) {
-      key[j] = score_key(x[j]);
-      if ((key[j] >> 20) >= b0) {
-        flags |= 1u << j;
-        c++;
-      }
-    }
+    for (int j = 0; j < 16; j++) key[j] = score_key(x[j]);
   } else {
 #pragma unroll
-    for (int j = 0; j < 16; j++) {
-      key[j] = e0 + j < vis ? score_key(srow[e0 + j]) : 0u;
-      if (e0 + j < vis && (key[j] >> 20) >= b0) {
-        flags |= 1u << j;
-        c++;
-      }
+    for (int j = 0; j < 16; j++) key[j] = e0 + j < vis ? score_key(srow[e0 + j]) : 0u;
+  }
+  // Threshold bin from the row's sample (identical in every workgroup): the
+  // whole row when it is short, else kSample / kSampleRun runs of kSampleRun
+  // consecutive elements, the first at 0 and the last ending at vis - 1.
+  for (int i = threadIdx.x; i < kBins0; i += blockDim.x) h[i] = 0u;
+  __syncthreads();
+  const int m = min(kSample, vis);
+  constexpr int kRuns = kSample / kSampleRun;
+  for (int i = threadIdx.x; i < m; i += blockDim.x) {
+    const int pos = vis <= kSample
+                        ? i
+                        : (int)((long)(i / kSampleRun) * (vis - kSampleRun) / (kRuns - 1)) + i % kSampleRun;
+    atomicAdd(&h[score_key(srow[pos]) >> 20], 1u);
+  }
+  __syncthreads();
+  const long expect = ((long)k * m + vis - 1) / vis;  // rank of the k-th key in the sample
+  const int r = (int)min((long)m, 2 * expect + 8);
+  find_bin(h, kBins0, r, res, tmp);
+  const uint32_t b0 = (uint32_t)res[0];
+  // Ordered compaction of this chunk's positions whose top digit is >= b0.
+  uint32_t flags = 0;
+  int c = 0;
+#pragma unroll
+  for (int j = 0; j < 16; j++) {
+    if (e0 + j < vis && (key[j] >> 20) >= b0) {
+      flags |= 1u << j;
+      c++;
     }
   }
   int total;
@@ -372,7 +423,7 @@ __global__ __launch_bounds__(kThreads) void topk_select(const float* __restrict_
                                                         int kv_len, int k,
                                                         const int32_t* __restrict__ k_rows,
                                                         int nchunks) {
-  __shared__ uint32_t h[kBins0 * (1 + kHistCopies)];
+  __shared__ __attribute__((aligned(16))) uint32_t h[kBins0 * (1 + kHistCopies)];
   __shared__ int32_t lpos[kLdsCap];
   __shared__ uint32_t lkey[kLdsCap];
   __shared__ int off[kTopkMaxChunks + 1];
@@ -453,7 +504,8 @@ __global__ __launch_bounds__(kThreads) void topk_select(const float* __restrict_
     n = histogram_and_candidates<true>(srow, vis, k, h, lpos, lkey, gpos, wtot, tmp, res, &b0, &above);
   else
     n = histogram_and_candidates<false>(srow, vis, k, h, lpos, lkey, gpos, wtot, tmp, res, &b0, &above);
-  select_and_emit(Cand{lpos, lkey, gpos, srow}, n, k - above, b0, h, res, tmp, out, k);
+  select_and_emit(Cand{lpos, lkey, gpos, srow}, n, k - above, b0 << 20, 1ull << 20, h, res, tmp,
+                  out, k);
 }
 
 }  // namespace

@@ -201,7 +201,10 @@ def score_rows(kind: str, B: int, T: int, L: int, seed: int, device="cpu") -> to
     "zeros" (all +0/-0, mixed), "relu" (half exact zeros, signed zeros mixed,
     rest Gaussian), "needle" (N(0,1) with 1% of entries +8), "const" (all 3.5),
     "desc" (strictly decreasing with position), "wide" (spans many octaves),
-    "strided" (every 64th position far above the rest).
+    "strided" (every 64th position far above the rest), "sampled" (far
+    above the rest exactly at the positions the top-k filter samples for its
+    threshold: 128 evenly spaced runs of 16, run j starting at
+    j * (L - 16) // 127; single-query rows, L > 2048).
     """
     g = _gen(seed, device)
     shape = (B, T, L)
@@ -229,6 +232,13 @@ def score_rows(kind: str, B: int, T: int, L: int, seed: int, device="cpu") -> to
         x = torch.randn(shape, generator=g, device=device)
         pos = torch.arange(L, device=device)
         return torch.where((pos % 64 == 0).expand(shape), torch.full_like(x, 100.0), x)
+    if kind == "sampled":
+        x = torch.randn(shape, generator=g, device=device)
+        hit = torch.zeros(L, dtype=torch.bool, device=device)
+        for j in range(128):
+            st = j * (L - 16) // 127
+            hit[st:st + 16] = True
+        return torch.where(hit.expand(shape), torch.full_like(x, 100.0), x)
     if kind == "wide":
         e = torch.randint(-60, 60, shape, generator=g, device=device).float()
         x = torch.randn(shape, generator=g, device=device)
