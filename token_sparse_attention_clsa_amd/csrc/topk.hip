@@ -381,12 +381,19 @@ __global__ __launch_bounds__(kFilterThreads) void topk_filter(const float* __res
   __syncthreads();
   const int m = min(kSample, vis);
   constexpr int kRuns = kSample / kSampleRun;
-  for (int i = threadIdx.x; i < m; i += blockDim.x) {
+  constexpr int kPer = kSample / kFilterThreads;  // sample elements per thread, all loaded at once
+  float sv[kPer];
+#pragma unroll
+  for (int j = 0; j < kPer; j++) {
+    const int i = threadIdx.x + j * kFilterThreads;
     const int pos = vis <= kSample
                         ? i
                         : (int)((long)(i / kSampleRun) * (vis - kSampleRun) / (kRuns - 1)) + i % kSampleRun;
-    atomicAdd(&h[score_key(srow[pos]) >> 20], 1u);
+    sv[j] = i < m ? srow[pos] : 0.f;
   }
+#pragma unroll
+  for (int j = 0; j < kPer; j++)
+    if (threadIdx.x + j * kFilterThreads < m) atomicAdd(&h[score_key(sv[j]) >> 20], 1u);
   __syncthreads();
   const long expect = ((long)k * m + vis - 1) / vis;  // rank of the k-th key in the sample
   const int r = (int)min((long)m, 2 * expect + 8);
