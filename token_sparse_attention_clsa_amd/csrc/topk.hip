@@ -51,8 +51,9 @@ constexpr int kHistCopies = 2;     // fallback histogram copies
 // takes the `per` consecutive bins below nbins - per * t (consecutive
 // threads, consecutive bins: no LDS bank conflicts); a wave scan, the wave
 // totals through tmp and one barrier give each thread the count above its
-// bins, and the thread where `need` falls walks them. Every thread of the
-// block must call it; need must be in [1, total]; tmp is int[16].
+// bins, and the thread where `need` falls walks them; res[2] = the count in
+// bin b. Every thread of the block must call it; need must be in [1, total];
+// tmp is int[16].
 __device__ void find_bin(const uint32_t* h, int nbins, int need, int* res, int* tmp) {
   const int per = (nbins + blockDim.x - 1) / blockDim.x;
   const int hi = nbins - 1 - (int)threadIdx.x * per;
@@ -74,6 +75,7 @@ __device__ void find_bin(const uint32_t* h, int nbins, int need, int* res, int* 
       if (acc + c >= need) {
         res[0] = hi - j;
         res[1] = acc;
+        res[2] = c;
         break;
       }
       acc += c;
@@ -142,11 +144,14 @@ struct SegCand {
 template <class Acc>
 __device__ void select_and_emit(const Acc& acc, int n, int need, uint32_t lo, uint64_t R,
                                 uint32_t* h, int* res, int* tmp, int32_t* out, int k) {
+  __shared__ uint32_t few[kWave];
+  __shared__ int nfew;
   while (R > 1) {  // uniform over the workgroup
     const int bits = 63 - __clzll(R);
     const int s = bits > 12 ? bits - 12 : 0;
     const int nb = (int)(R >> s);
     for (int i = threadIdx.x; i < nb; i += blockDim.x) h[i] = 0u;
+    if (threadIdx.x == 0) nfew = 0;
     __syncthreads();
     for (int i = threadIdx.x; i < n; i += blockDim.x) {
       const uint32_t key = acc.k(i);
@@ -159,6 +164,35 @@ __device__ void select_and_emit(const Acc& acc, int n, int need, uint32_t lo, ui
     lo += (uint32_t)res[0] << s;
     need -= res[1];
     R = 1ull << s;
+    if (R > 1 && res[2] <= kWave) {
+      // At most 64 keys left in [lo, lo + R): one wave ranks them (keys
+      // strictly above and equal to each) instead of further passes.
+      const int cnt = res[2];
+      for (int i = threadIdx.x; i < n; i += blockDim.x) {
+        const uint32_t key = acc.k(i);
+        if (key >= lo && (uint64_t)(key - lo) < R) few[atomicAdd(&nfew, 1)] = key;
+      }
+      __syncthreads();
+      if (threadIdx.x < kWave) {
+        const int lane = threadIdx.x;
+        const uint32_t v = lane < cnt ? few[lane] : 0u;
+        int gt = 0, eq = 0;
+        for (int j = 0; j < cnt; j++) {  // uniform
+          const uint32_t o = (uint32_t)__builtin_amdgcn_readlane((int)v, j);
+          gt += o > v;
+          eq += o == v;
+        }
+        const unsigned long long hit = __ballot(lane < cnt && gt < need && need <= gt + eq);
+        if (lane == __builtin_ctzll(hit)) {
+          res[0] = (int)v;     // theta
+          res[1] = need - gt;  // keys equal to theta still to take
+        }
+      }
+      __syncthreads();
+      lo = (uint32_t)res[0];
+      need = res[1];
+      R = 1;
+    }
   }
   const uint32_t theta = lo;
   const int quota = need;  // how many keys equal to theta are taken
@@ -199,20 +233,22 @@ __device__ void select_and_emit(const Acc& acc, int n, int need, uint32_t lo, ui
   }
 }
 
-// Selection of the k largest among n >= k candidates. The radix passes run
-// on key - min over the candidates' own key range, so the first pass spreads
-// them over its bins even when they share the top bits of their keys, and a
-// range of at most 2^24 keys takes two passes.
+// Selection of the k largest among n >= k candidates whose keys lie in
+// [mn, mx]. The radix passes run on key - mn over the candidates' own key
+// range, so the first pass spreads them over its bins even when they share
+// the top bits of their keys; a range of at most 2^24 keys takes two passes,
+// or one when the bin it leaves holds at most 64 keys.
 template <class Acc>
-__device__ void select_top(const Acc& acc, int n, int k, uint32_t* h, int* res, int* tmp,
-                           int32_t* out) {
-  __shared__ uint32_t mm[2][kWaves];
-  uint32_t mn = 0xffffffffu, mx = 0u;
-  for (int i = threadIdx.x; i < n; i += blockDim.x) {
-    const uint32_t key = acc.k(i);
-    mn = min(mn, key);
-    mx = max(mx, key);
-  }
+__device__ void select_top(const Acc& acc, int n, int k, uint32_t mn, uint32_t mx, uint32_t* h,
+                           int* res, int* tmp, int32_t* out) {
+  const uint64_t span = (uint64_t)(mx - mn) + 1;  // n >= k >= 1, so mx >= mn
+  const uint64_t R = span == 1 ? 1 : 1ull << (64 - __clzll(span - 1));
+  select_and_emit(acc, n, k, mn, R, h, res, tmp, out, k);
+}
+
+// Block-wide min and max of the threads' (mn, mx); ends with a barrier
+// (the writes before it, e.g. an LDS gather, are visible after it).
+__device__ void block_minmax(uint32_t& mn, uint32_t& mx, uint32_t (*mm)[kWaves]) {
   mn = wave_min_u32(mn);
   mx = wave_max_u32(mx);
   const int wave = threadIdx.x / kWave, nw = blockDim.x / kWave;
@@ -225,9 +261,6 @@ __device__ void select_top(const Acc& acc, int n, int k, uint32_t* h, int* res, 
     mn = min(mn, mm[0][w]);
     mx = max(mx, mm[1][w]);
   }
-  const uint64_t span = (uint64_t)(mx - mn) + 1;  // n >= k >= 1, so mx >= mn
-  const uint64_t R = span == 1 ? 1 : 1ull << (64 - __clzll(span - 1));
-  select_and_emit(acc, n, k, mn, R, h, res, tmp, out, k);
 }
 
 template <bool VEC>
@@ -349,7 +382,7 @@ __global__ __launch_bounds__(kFilterThreads) void topk_filter(const float* __res
                                                               int nchunks) {
   __shared__ __attribute__((aligned(16))) uint32_t h[kBins0];
   __shared__ int tmp[17];
-  __shared__ int res[2];
+  __shared__ int res[3];
   const int row = blockIdx.y;
   const int vis = kv_len - T + (row % T) + 1;
   const int c0 = blockIdx.x * kChunk;
@@ -434,9 +467,10 @@ __global__ __launch_bounds__(kThreads) void topk_select(const float* __restrict_
   __shared__ int32_t lpos[kLdsCap];
   __shared__ uint32_t lkey[kLdsCap];
   __shared__ int off[kTopkMaxChunks + 1];
+  __shared__ uint32_t mm[2][kWaves];
   __shared__ int wtot[kWaves + 1];
   __shared__ int tmp[17];
-  __shared__ int res[2];
+  __shared__ int res[3];
   const int row = blockIdx.x;
   const int vis = kv_len - T + (row % T) + 1;
   int32_t* out = idx + (size_t)row * k;  // k slots
@@ -478,6 +512,7 @@ __global__ __launch_bounds__(kThreads) void topk_select(const float* __restrict_
     overflow = __syncthreads_or(v > kTopkSegCap) != 0;
   }
   if (n >= k && !overflow) {
+    uint32_t mn = 0xffffffffu, mx = 0u;  // key range of the candidates
     if (n <= kLdsCap) {
       if (gc < nchunks) {
         const int o = off[gc], cnt = off[gc + 1] - off[gc];
@@ -487,18 +522,29 @@ __global__ __launch_bounds__(kThreads) void topk_select(const float* __restrict_
           if (j < cnt) {
             lpos[o + j] = pre[u].x;
             lkey[o + j] = (uint32_t)pre[u].y;
+            mn = min(mn, (uint32_t)pre[u].y);
+            mx = max(mx, (uint32_t)pre[u].y);
           }
         }
         for (int j = j0 + kSpec * tpc; j < cnt; j += tpc) {
           const int2 e = sg[j];
           lpos[o + j] = e.x;
           lkey[o + j] = (uint32_t)e.y;
+          mn = min(mn, (uint32_t)e.y);
+          mx = max(mx, (uint32_t)e.y);
         }
       }
-      __syncthreads();
-      select_top(Cand{lpos, lkey, nullptr, srow}, n, k, h, res, tmp, out);
+      block_minmax(mn, mx, mm);  // its barrier also publishes the gather
+      select_top(Cand{lpos, lkey, nullptr, srow}, n, k, mn, mx, h, res, tmp, out);
     } else {
-      select_top(SegCand{segs, off, nchunks}, n, k, h, res, tmp, out);
+      const SegCand acc{segs, off, nchunks};
+      for (int i = threadIdx.x; i < n; i += blockDim.x) {
+        const uint32_t key = acc.k(i);
+        mn = min(mn, key);
+        mx = max(mx, key);
+      }
+      block_minmax(mn, mx, mm);
+      select_top(acc, n, k, mn, mx, h, res, tmp, out);
     }
     return;
   }
