@@ -625,11 +625,16 @@ __global__ __launch_bounds__(kD) void attn_combine_kernel(const float* __restric
   if (d == 0 && lse) lse[head] = L > 0.f ? (M + log2f(L)) * kLn2 : -INFINITY;
 }
 
-// Waves per workgroup: the largest divisor of Hkv that is at most kMaxWaves.
-// KV heads per workgroup: the largest divisor of Hkv with W waves each
-// fitting the workgroup.
+// KV heads per workgroup. One wave per head (W = 1): the largest divisor of
+// Hkv up to kMaxWaves, so a workgroup reads whole token rows. W waves per
+// head: the largest divisor with at most 4 waves per workgroup, since the
+// merge barrier makes each wave wait for the slowest wave of its workgroup
+// (measured on the 128K decode, W = 4: 10.94 us per call with one head per
+// workgroup vs 11.2 us with two; W = 2: 11.5 us with two heads vs 13.6 us
+// with one).
 int heads_per_block(int Hkv, int W) {
-  for (int h = kMaxWaves / W; h > 1; h--)
+  const int cap = W == 1 ? kMaxWaves : (W < 4 ? 4 / W : 1);
+  for (int h = cap; h > 1; h--)
     if (Hkv % h == 0) return h;
   return 1;
 }
