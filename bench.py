@@ -11,10 +11,13 @@ inputs resident in HBM before the timed region starts.
 
 Prints one JSON line: tokens/s for the step (K timed steps, nothing enqueued
 between them), the step's spread and its cold-cache time, and the roofline
-of the dominant kernel, the sparse-attention call: algorithmic bytes over
-its GPU time per call (back-to-back calls replayed from a HIP graph between
-one event pair), warm and with the caches evicted before each call, plus the
-HBM traffic rocprofv3 measured for it; per-kernel times; a dense-gather run
+of the dominant kernel (the one with the larger share of the step): for the
+sparse-attention call, algorithmic bytes (decode) or flops (chunk) over its
+GPU time per call (back-to-back calls replayed from a HIP graph between one
+event pair), warm and with the caches evicted before each call, plus the
+HBM traffic rocprofv3 measured for it; for a chunk's indexer, its flops over
+its time per call, with the attention call's figures nested beside it;
+per-kernel times; a dense-gather run
 of the same call (k = kv_len) for the speedup; and the CPU oracle timed on
 one pinned host core on a bounded sample of the same workload.
 
@@ -32,6 +35,7 @@ import time
 
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 matrix cores
+MFMA_FP8_PEAK_TFLOPS = 5000.0    # MI355X dense fp8 matrix cores
 ROOT = os.path.dirname(os.path.abspath(__file__))
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "sparse_attn_decode128k_traffic.txt")
 ATTN_SOURCE = os.path.join(ROOT, "token_sparse_attention_clsa_amd", "csrc", "sparse_attn.hip")
@@ -411,26 +415,45 @@ def main():
             "sparse_attn_us": us_attn,
         }
 
-    # Roofline of the dominant kernel, the sparse-attention call. A decode
-    # query gathers its own rows once per layer: HBM-bound, priced by the
-    # algorithmic bytes. In a chunk, the queries' index rows overlap and the
-    # repeated gathers are served by L2 / Infinity Cache, so the call is
-    # priced by its bf16 matrix-core flops instead (q.K and P.V: 4 flops per
-    # (query head, entry, element)).
+    # Roofline of the sparse-attention call. A decode query gathers its own
+    # rows once per layer: HBM-bound, priced by the algorithmic bytes. In a
+    # chunk, the queries' index rows overlap and the repeated gathers are
+    # served by L2 / Infinity Cache, so the call is priced by its bf16
+    # matrix-core flops instead (q.K and P.V: 4 flops per (query head, entry,
+    # element)).
     if wl.T == 1:
-        roofline = {"bound": "hbm", "achieved": attn_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                    "frac": attn_gbs / HBM_PEAK_GBS, "traffic": measured_traffic(wl.name)}
+        attn_roof = {"bound": "hbm", "achieved": attn_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": attn_gbs / HBM_PEAK_GBS, "traffic": measured_traffic(wl.name)}
     else:
         attn_tflops = 4.0 * wl.B * wl.T * wl.k * wl.Hq * wl.D / (us_attn * 1e-6) / 1e12
-        roofline = {"bound": "mfma", "achieved": attn_tflops, "peak": MFMA_BF16_PEAK_TFLOPS,
-                    "unit": "TFLOP/s", "frac": attn_tflops / MFMA_BF16_PEAK_TFLOPS, "traffic": None}
+        attn_roof = {"bound": "mfma", "achieved": attn_tflops, "peak": MFMA_BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": attn_tflops / MFMA_BF16_PEAK_TFLOPS, "traffic": None}
     split_kernel = "attn_split_mfma" if wl.dtype == 1 else "attn_split_kernel"
-    roofline.update({"kernel": f"sparse_attn call ({split_kernel} + attn_combine_kernel)",
-                     "bytes_per_launch": alg["sparse_attn"], "avg_launch_us": us_attn,
-                     "cold_launch_us": us_attn_cold})
+    attn_roof.update({"kernel": f"sparse_attn call ({split_kernel} + attn_combine_kernel)",
+                      "bytes_per_launch": alg["sparse_attn"], "avg_launch_us": us_attn,
+                      "cold_launch_us": us_attn_cold})
     if wl.T == 1:
         cold_gbs = alg["sparse_attn"] / (us_attn_cold * 1e-6) / 1e9
-        roofline.update({"cold_achieved": cold_gbs, "cold_frac": cold_gbs / HBM_PEAK_GBS})
+        attn_roof.update({"cold_achieved": cold_gbs, "cold_frac": cold_gbs / HBM_PEAK_GBS})
+    # The dominant kernel is the one with the larger share of the step: the
+    # attention call (n layers) or the indexer (F layers). A chunk's indexer
+    # is a contraction priced by its flops (2 * H_I * D_I per visible key);
+    # a decode indexer streams its keys and is priced by its bytes.
+    roofline = attn_roof
+    if us_index * len(wl.f_layers) > us_attn * n and wl.idx_dtype != 0:
+        vis_keys = wl.B * sum(wl.kv_len - wl.T + t + 1 for t in range(wl.T))
+        if wl.T > 1:
+            tf = 2.0 * wl.H_I * wl.D_I * vis_keys / (us_index * 1e-6) / 1e12
+            peak = MFMA_FP8_PEAK_TFLOPS if wl.idx_dtype == 2 else MFMA_BF16_PEAK_TFLOPS
+            roofline = {"bound": "mfma", "achieved": tf, "peak": peak, "unit": "TFLOP/s",
+                        "frac": tf / peak, "traffic": None}
+        else:
+            gbs = alg["index_score"] / (us_index * 1e-6) / 1e9
+            roofline = {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                        "frac": gbs / HBM_PEAK_GBS, "traffic": None}
+        kname = "idx_score_multi" if wl.T >= 8 else "idx_score_mfma"
+        roofline.update({"kernel": f"index_score ({kname})", "avg_launch_us": us_index,
+                         "sparse_attn": attn_roof})
 
     tokens_per_step = wl.B * wl.T
     result = {
