@@ -135,14 +135,28 @@ __global__ __launch_bounds__(kIdxThreads) void idx_score_mfma(
 
 // Multi-query form (chunked prefill): a workgroup of kQB waves takes kQB
 // consecutive queries of one batch element (wave w = query t0 + w, its heads
-// in VGPRs as above) and a range of keys. Key tiles of kKT keys are copied
-// from global memory into LDS once per workgroup (double-buffered, rows padded
-// to D_I*elt + 16 bytes so the 16 rows one B-fragment read touches fall in
-// distinct banks) and every wave runs its MFMAs on the shared tile, so each
-// key row leaves L2 once per kQB queries instead of once per query.
+// in VGPRs as above) and a range of keys. Key tiles of kKT keys move from
+// global memory straight into LDS (global_load_lds, 16 bytes per lane, no
+// staging registers), double-buffered in two separate LDS objects so the
+// compiler's wait analysis keeps a transfer into one buffer apart from reads
+// of the other; every wave runs its MFMAs on the shared tile, so each key row
+// leaves L2 once per kQB queries instead of once per query. Within the rows
+// of each 256-byte span the 16-byte chunks are XOR-swizzled by row, so the 16
+// rows one B-fragment read touches fall in distinct banks. A tile's scores
+// are stored at the top of the next iteration, after its transfer is issued,
+// so the per-tile wait for the transfer rarely waits on a store.
 // grid (key_splits, B * ceil(T / kQB)), block kQB * 64.
 constexpr int kQB = 8;
 constexpr int kKT = 64;
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Sum over the four 16-lane groups (lanes l, l^16, l^32, l^48).
+__device__ __forceinline__ float group4_sum(float v) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
 
 template <int DT, int DI, int HI>
 __global__ __launch_bounds__(kQB * kWave) void idx_score_multi(
@@ -152,11 +166,13 @@ __global__ __launch_bounds__(kQB * kWave) void idx_score_multi(
   using E = IdxElem<DT>;
   constexpr int NS = DI / 32;
   constexpr int NH = HI / 16;
-  constexpr int ROWB = DI * E::bytes;        // bytes of one key row
-  constexpr int PITCH = ROWB + 16;           // padded LDS row
-  constexpr int CHUNKS = ROWB / 16;          // 16-byte chunks per row
-  constexpr int TILE_CHUNKS = kKT * CHUNKS;  // per tile
-  __shared__ __attribute__((aligned(16))) uint8_t tile[2][kKT * PITCH];
+  constexpr int ROWB = DI * E::bytes;          // bytes of one key row: 64, 128 or 256
+  constexpr int CHUNKS = ROWB / 16;            // 16-byte chunks per row
+  constexpr int RPS = 256 / ROWB;              // rows per 256-byte span
+  constexpr int NI = kKT * ROWB / 1024;        // 1 KiB transfers per tile
+  static_assert(ROWB >= 64 && ROWB <= 256 && NI >= 1, "row size");
+  __shared__ __attribute__((aligned(16))) uint8_t tile0[kKT * ROWB];
+  __shared__ __attribute__((aligned(16))) uint8_t tile1[kKT * ROWB];
 
   const int lane = threadIdx.x % kWave;
   const int wave = threadIdx.x / kWave;
@@ -189,73 +205,67 @@ __global__ __launch_bounds__(kQB * kWave) void idx_score_multi(
   const int k1 = min(k0 + keys_per_split, kv_len);
   const int kend = min(k1, vis_max);  // keys any query of the group sees
 
-  // Global -> registers -> LDS: each thread moves chunks c0 and c1 (16 bytes each).
-  static_assert(TILE_CHUNKS <= 2 * kQB * kWave, "two staged chunks per thread");
-  const int c0 = threadIdx.x, c1 = threadIdx.x + kQB * kWave;
-  uint4 st0 = {0, 0, 0, 0}, st1 = {0, 0, 0, 0};
-#define CLSA_FETCH(key0)                                                                      \
-  {                                                                                           \
-    if (c0 < TILE_CHUNKS)                                                                     \
-      st0 = *reinterpret_cast<const uint4*>(                                                  \
-          kbase + (size_t)min((key0) + c0 / CHUNKS, kv_len - 1) * ROWB + (c0 % CHUNKS) * 16); \
-    if (c1 < TILE_CHUNKS)                                                                     \
-      st1 = *reinterpret_cast<const uint4*>(                                                  \
-          kbase + (size_t)min((key0) + c1 / CHUNKS, kv_len - 1) * ROWB + (c1 % CHUNKS) * 16); \
-  }
-#define CLSA_COMMIT(buf)                                                                           \
-  {                                                                                                \
-    if (c0 < TILE_CHUNKS)                                                                          \
-      *reinterpret_cast<uint4*>(&tile[buf][(c0 / CHUNKS) * PITCH + (c0 % CHUNKS) * 16]) = st0;      \
-    if (c1 < TILE_CHUNKS)                                                                          \
-      *reinterpret_cast<uint4*>(&tile[buf][(c1 / CHUNKS) * PITCH + (c1 % CHUNKS) * 16]) = st1;      \
-  }
-
   // Keys past the group's visible range are written as -inf without compute.
-  for (int key = max(k0, kend) + threadIdx.x % kWave; key < k1; key += kWave)
+  for (int key = max(k0, kend) + lane; key < k1; key += kWave)
     if (active) srow[key] = -INFINITY;
   if (k0 >= kend) return;  // uniform over the workgroup
 
-  CLSA_FETCH(k0)
-  CLSA_COMMIT(0)
-  __syncthreads();
-  int buf = 0;
-  for (int base = k0; base < kend; base += kKT) {  // uniform over the workgroup
-    const bool more = base + kKT < kend;
-    if (more) {
-      CLSA_FETCH(base + kKT)  // in flight while this tile is computed
-    }
-    float res = 0.f;
-#pragma unroll
-    for (int j = 0; j < kKT / 16; j++) {
-      f32x4 acc[NH];
-#pragma unroll
-      for (int ht = 0; ht < NH; ht++) acc[ht] = f32x4{0.f, 0.f, 0.f, 0.f};
-      const uint8_t* rowp = &tile[buf][(j * 16 + col) * PITCH + grp * (ROWB / 4)];
-#pragma unroll
-      for (int s = 0; s < NS; s++) {
-        const typename E::frag bf = E::load(rowp + 8 * s * E::bytes);
-#pragma unroll
-        for (int ht = 0; ht < NH; ht++) acc[ht] = E::mfma(a[ht][s], bf, acc[ht]);
-      }
-      float v = 0.f;
-#pragma unroll
-      for (int ht = 0; ht < NH; ht++)
-#pragma unroll
-        for (int r = 0; r < 4; r++) v += wv[ht][r] * fmaxf(acc[ht][r], 0.f);
-      v += __shfl_xor(v, 16, kWave);
-      v += __shfl_xor(v, 32, kWave);
-      if (grp == j) res = v;
-    }
-    const int key_out = base + grp * 16 + col;
-    if (active && key_out < k1) srow[key_out] = key_out < vis ? res : -INFINITY;
-    if (more) {
-      CLSA_COMMIT(buf ^ 1)
-      __syncthreads();  // next tile visible; everyone is done with this one
-      buf ^= 1;
-    }
+  // LDS byte offset of logical 16-byte chunk c of tile row r.
+#define CLSA_CHUNK_AT(r, c) ((r) * ROWB + 16 * ((c) ^ (((r) / RPS) & (CHUNKS - 1))))
+  // Tile of keys key0 .. key0 + kKT - 1 into buffer BUF: transfer m carries
+  // tile bytes [1024 m, 1024 m + 1024), lane L the 16 bytes at 1024 m + 16 L,
+  // i.e. row (1024 m + 16 L) / ROWB, physical chunk L % CHUNKS, which holds
+  // the row's logical chunk (L % CHUNKS) ^ swizzle(row). Keys past kv_len
+  // read the last key (their scores are not stored).
+#define CLSA_ISSUE(key0, BUF)                                                                         \
+  for (int m = wave; m < NI; m += kQB) {                                                              \
+    const int r = (1024 * m + 16 * lane) / ROWB;                                                      \
+    const int c = (lane % CHUNKS) ^ ((r / RPS) & (CHUNKS - 1));                                       \
+    const uint8_t* src = kbase + (size_t)min((key0) + r, kv_len - 1) * ROWB + 16 * c;                \
+    __builtin_amdgcn_global_load_lds(src, (lds_void*)((BUF) + 1024 * m), 16, 0, 0);                  \
   }
-#undef CLSA_FETCH
-#undef CLSA_COMMIT
+  // Tile at key `base` from buffer CUR, after the transfer of the next tile
+  // into NXT is issued and the previous tile's scores are stored. The wait +
+  // barrier make this tile's transfers (every wave's) visible and guarantee
+  // every wave is done with NXT, which held the previous tile.
+#define CLSA_TILE(base, CUR, NXT)                                                                     \
+  {                                                                                                   \
+    __builtin_amdgcn_s_waitcnt(0x0070); /* vmcnt(0) lgkmcnt(0) */                                    \
+    asm volatile("s_barrier" ::: "memory");                                                           \
+    if ((base) + kKT < kend) { CLSA_ISSUE((base) + kKT, NXT) }                                        \
+    if (active && prev_key < k1) srow[prev_key] = prev_key < vis ? prev_res : -INFINITY;              \
+    float res = 0.f;                                                                                  \
+    _Pragma("unroll") for (int j = 0; j < kKT / 16; j++) {                                            \
+      f32x4 acc[NH];                                                                                  \
+      _Pragma("unroll") for (int ht = 0; ht < NH; ht++) acc[ht] = f32x4{0.f, 0.f, 0.f, 0.f};         \
+      const int r = j * 16 + col;                                                                     \
+      _Pragma("unroll") for (int s = 0; s < NS; s++) {                                                \
+        const int off = grp * (ROWB / 4) + 8 * s * E::bytes;                                          \
+        const typename E::frag bf = E::load((CUR) + CLSA_CHUNK_AT(r, off / 16) + off % 16);           \
+        _Pragma("unroll") for (int ht = 0; ht < NH; ht++) acc[ht] = E::mfma(a[ht][s], bf, acc[ht]);   \
+      }                                                                                               \
+      float v = 0.f;                                                                                  \
+      _Pragma("unroll") for (int ht = 0; ht < NH; ht++)                                               \
+        _Pragma("unroll") for (int q = 0; q < 4; q++) v += wv[ht][q] * fmaxf(acc[ht][q], 0.f);       \
+      v = group4_sum(v);                                                                              \
+      if (grp == j) res = v;                                                                          \
+    }                                                                                                 \
+    prev_key = (base) + grp * 16 + col;                                                               \
+    prev_res = res;                                                                                   \
+  }
+
+  int prev_key = k1;  // nothing to store before the first tile
+  float prev_res = 0.f;
+  CLSA_ISSUE(k0, tile0)
+  for (int base = k0; base < kend; base += 2 * kKT) {  // uniform over the workgroup
+    CLSA_TILE(base, tile0, tile1)
+    if (base + kKT >= kend) break;
+    CLSA_TILE(base + kKT, tile1, tile0)
+  }
+  if (active && prev_key < k1) srow[prev_key] = prev_key < vis ? prev_res : -INFINITY;
+#undef CLSA_TILE
+#undef CLSA_ISSUE
+#undef CLSA_CHUNK_AT
 }
 
 // Float32 indexer (small head counts): one thread per key, the query's heads
