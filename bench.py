@@ -352,6 +352,20 @@ def main():
                                                       ws=attn_ws), 20)
     us_step_cold = cold_us(lambda i: step.run(), 10)
 
+    # Measured memory ceiling on this device: a plain device-to-device copy of
+    # 256 MiB (torch's copy kernel), bytes read + written over its time.
+    csrc = scratch[: 1 << 26]
+    cdst = scratch[1 << 26: 2 << 26]
+    for _ in range(3):
+        cdst.copy_(csrc)
+    a_ev, b_ev = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a_ev.record()
+    for _ in range(10):
+        cdst.copy_(csrc)
+    b_ev.record()
+    torch.cuda.synchronize()
+    copy_gbs = 2 * csrc.numel() * 4 * 10 / (a_ev.elapsed_time(b_ev) * 1e-3) / 1e9
+
     # Per-step spread: one event before each of K steps (none between kernels).
     evs = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
     torch.cuda.synchronize()
@@ -434,7 +448,8 @@ def main():
                       "cold_launch_us": us_attn_cold})
     if wl.T == 1:
         cold_gbs = alg["sparse_attn"] / (us_attn_cold * 1e-6) / 1e9
-        attn_roof.update({"cold_achieved": cold_gbs, "cold_frac": cold_gbs / HBM_PEAK_GBS})
+        attn_roof.update({"cold_achieved": cold_gbs, "cold_frac": cold_gbs / HBM_PEAK_GBS,
+                          "measured_copy_gbs": copy_gbs, "frac_of_measured_copy": attn_gbs / copy_gbs})
     # The dominant kernel is the one with the larger share of the step: the
     # attention call (n layers) or the indexer (F layers). A chunk's indexer
     # is a contraction priced by its flops (2 * H_I * D_I per visible key);
