@@ -10,12 +10,12 @@
 //   1. topk_filter (chunks x rows, 256 threads): every workgroup of a row
 //      takes the same deterministic sample of the row (128 runs of 16
 //      consecutive elements, evenly spaced, so the sample costs 128 cache
-//      lines rather than 2048), histograms the sample's top digits in LDS
-//      and picks the bin where the sample's count from the top reaches about
-//      twice the rank k would have in the sample. It then writes, in
-//      position order, the (position, key) pairs of its 4096-element chunk
-//      whose top digit is at or above that bin (at most kTopkSegCap of them)
-//      and their count. With a 2048-element sample the chance that this
+//      lines rather than 2048), histograms the sample's keys over their own
+//      range in LDS and picks the bin where the sample's count from the top
+//      reaches about twice the rank k would have in the sample; the bin's
+//      lower bound is the threshold key. It then writes, in position order,
+//      the (position, key) pairs of its 4096-element chunk at or above the
+//      threshold (at most kTopkSegCap of them) and their count. With a 2048-element sample the chance that this
 //      keeps fewer than k positions, or more than the cap in a chunk, is
 //      negligible for any smooth score distribution, and the next kernel
 //      checks both anyway.
@@ -383,6 +383,7 @@ __global__ __launch_bounds__(kFilterThreads) void topk_filter(const float* __res
   __shared__ __attribute__((aligned(16))) uint32_t h[kBins0];
   __shared__ int tmp[17];
   __shared__ int res[3];
+  __shared__ uint32_t fmm[2][kFilterThreads / kWave];
   const int row = blockIdx.y;
   const int vis = kv_len - T + (row % T) + 1;
   const int c0 = blockIdx.x * kChunk;
@@ -407,11 +408,12 @@ __global__ __launch_bounds__(kFilterThreads) void topk_filter(const float* __res
 #pragma unroll
     for (int j = 0; j < 16; j++) key[j] = e0 + j < vis ? score_key(srow[e0 + j]) : 0u;
   }
-  // Threshold bin from the row's sample (identical in every workgroup): the
+  // Threshold from the row's sample (identical in every workgroup): the
   // whole row when it is short, else kSample / kSampleRun runs of kSampleRun
-  // consecutive elements, the first at 0 and the last ending at vis - 1.
-  for (int i = threadIdx.x; i < kBins0; i += blockDim.x) h[i] = 0u;
-  __syncthreads();
+  // consecutive elements, the first at 0 and the last ending at vis - 1. The
+  // sample's keys are binned over their own range (key - min, at most 4096
+  // bins), so the threshold stays close to the target rank however narrow
+  // the score distribution is.
   const int m = min(kSample, vis);
   constexpr int kRuns = kSample / kSampleRun;
   constexpr int kPer = kSample / kFilterThreads;  // sample elements per thread, all loaded at once
@@ -424,20 +426,48 @@ __global__ __launch_bounds__(kFilterThreads) void topk_filter(const float* __res
                         : (int)((long)(i / kSampleRun) * (vis - kSampleRun) / (kRuns - 1)) + i % kSampleRun;
     sv[j] = i < m ? srow[pos] : 0.f;
   }
+  uint32_t sk[kPer];
+  uint32_t mn = 0xffffffffu, mx = 0u;
+#pragma unroll
+  for (int j = 0; j < kPer; j++) {
+    sk[j] = score_key(sv[j]);
+    if (threadIdx.x + j * kFilterThreads < m) {
+      mn = min(mn, sk[j]);
+      mx = max(mx, sk[j]);
+    }
+  }
+  mn = wave_min_u32(mn);
+  mx = wave_max_u32(mx);
+  const int wave = threadIdx.x / kWave;
+  if (threadIdx.x % kWave == 0) {
+    fmm[0][wave] = mn;
+    fmm[1][wave] = mx;
+  }
+  for (int i = threadIdx.x; i < kBins0; i += blockDim.x) h[i] = 0u;
+  __syncthreads();
+#pragma unroll
+  for (int w = 0; w < kFilterThreads / kWave; w++) {
+    mn = min(mn, fmm[0][w]);
+    mx = max(mx, fmm[1][w]);
+  }
+  const uint64_t span = (uint64_t)(mx - mn) + 1;
+  const int bits = span == 1 ? 0 : 64 - __clzll(span - 1);  // range 2^bits covers the sample
+  const int sh = bits > 12 ? bits - 12 : 0;
+  const int nb = 1 << (bits - sh);
 #pragma unroll
   for (int j = 0; j < kPer; j++)
-    if (threadIdx.x + j * kFilterThreads < m) atomicAdd(&h[score_key(sv[j]) >> 20], 1u);
+    if (threadIdx.x + j * kFilterThreads < m) atomicAdd(&h[(sk[j] - mn) >> sh], 1u);
   __syncthreads();
   const long expect = ((long)k * m + vis - 1) / vis;  // rank of the k-th key in the sample
   const int r = (int)min((long)m, 2 * expect + 8);
-  find_bin(h, kBins0, r, res, tmp);
-  const uint32_t b0 = (uint32_t)res[0];
-  // Ordered compaction of this chunk's positions whose top digit is >= b0.
+  find_bin(h, nb, r, res, tmp);
+  const uint32_t thr = mn + ((uint32_t)res[0] << sh);
+  // Ordered compaction of this chunk's positions whose key is >= thr.
   uint32_t flags = 0;
   int c = 0;
 #pragma unroll
   for (int j = 0; j < 16; j++) {
-    if (e0 + j < vis && (key[j] >> 20) >= b0) {
+    if (e0 + j < vis && key[j] >= thr) {
       flags |= 1u << j;
       c++;
     }
