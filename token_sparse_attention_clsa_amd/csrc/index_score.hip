@@ -30,6 +30,12 @@ namespace {
 constexpr int kIdxThreads = 256;  // 4 waves
 constexpr int kKeysPerWaveIter = 64;  // 4 MFMA tiles of 16 keys
 
+// max(x, 0) on the bit pattern: a non-negative float's bits are a
+// non-negative int and a negative one's (-0 included) a negative int, so the
+// signed integer max with 0 is ReLU for every non-NaN input in one
+// v_max_i32 (fmaxf in IEEE mode also quiets its operand first).
+__device__ __forceinline__ float relu(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
+
 template <int DT>
 struct IdxElem;
 template <>
@@ -124,7 +130,7 @@ __global__ __launch_bounds__(kIdxThreads) void idx_score_mfma(
 #pragma unroll
       for (int ht = 0; ht < NH; ht++)
 #pragma unroll
-        for (int r = 0; r < 4; r++) v += wv[ht][r] * fmaxf(acc[ht][r], 0.f);
+        for (int r = 0; r < 4; r++) v += wv[ht][r] * relu(acc[ht][r]);
       v += __shfl_xor(v, 16, kWave);
       v += __shfl_xor(v, 32, kWave);
       if (grp == j) res = v;
@@ -246,7 +252,7 @@ __global__ __launch_bounds__(kQB * kWave) void idx_score_multi(
       }                                                                                               \
       float v = 0.f;                                                                                  \
       _Pragma("unroll") for (int ht = 0; ht < NH; ht++)                                               \
-        _Pragma("unroll") for (int q = 0; q < 4; q++) v += wv[ht][q] * fmaxf(acc[ht][q], 0.f);       \
+        _Pragma("unroll") for (int q = 0; q < 4; q++) v += wv[ht][q] * relu(acc[ht][q]);       \
       v = group4_sum(v);                                                                              \
       if (grp == j) res = v;                                                                          \
     }                                                                                                 \
