@@ -156,12 +156,17 @@ constexpr int kQB = 8;
 constexpr int kKT = 64;
 typedef __attribute__((address_space(3))) void lds_void;
 
-// Sum over the four 16-lane groups (lanes l, l^16, l^32, l^48).
-__device__ __forceinline__ float group4_sum(float v) {
-  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
-  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+// Lane group g (lanes 16 g .. 16 g + 15) receives v_g summed over the four
+// lane groups (lanes l, l^16, l^32, l^48, added in that pairing order): a
+// 4 x 4 transpose-reduce in three lane swaps and three adds.
+__device__ __forceinline__ float group4_transpose_sum(float v0, float v1, float v2, float v3) {
+  // Upper half receives the lower half's v2 / v3, lower half the upper's v0 / v1.
+  const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(v0), __float_as_uint(v2), false, false);
+  const auto q = __builtin_amdgcn_permlane32_swap(__float_as_uint(v1), __float_as_uint(v3), false, false);
+  const float x02 = __uint_as_float(p[0]) + __uint_as_float(p[1]);  // lower: v0 sum, upper: v2 sum
+  const float x13 = __uint_as_float(q[0]) + __uint_as_float(q[1]);  // lower: v1 sum, upper: v3 sum
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x02), __float_as_uint(x13), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 template <int DT, int DI, int HI>
@@ -240,10 +245,10 @@ __global__ __launch_bounds__(kQB * kWave) void idx_score_multi(
     asm volatile("s_barrier" ::: "memory");                                                           \
     if ((base) + kKT < kend) { CLSA_ISSUE((base) + kKT, NXT) }                                        \
     if (active && prev_key < k1) srow[prev_key] = prev_key < vis ? prev_res : -INFINITY;              \
-    float res = 0.f;                                                                                  \
+    float vs[kKT / 16];                                                                               \
     _Pragma("unroll") for (int j = 0; j < kKT / 16; j++) {                                            \
       f32x4 acc[NH];                                                                                  \
-      _Pragma("unroll") for (int ht = 0; ht < NH; ht++) acc[ht] = f32x4{0.f, 0.f, 0.f, 0.f};         \
+      _Pragma("unroll") for (int ht = 0; ht < NH; ht++) acc[ht] = f32x4{0.f, 0.f, 0.f, 0.f};          \
       const int r = j * 16 + col;                                                                     \
       _Pragma("unroll") for (int s = 0; s < NS; s++) {                                                \
         const int off = grp * (ROWB / 4) + 8 * s * E::bytes;                                          \
@@ -252,10 +257,10 @@ __global__ __launch_bounds__(kQB * kWave) void idx_score_multi(
       }                                                                                               \
       float v = 0.f;                                                                                  \
       _Pragma("unroll") for (int ht = 0; ht < NH; ht++)                                               \
-        _Pragma("unroll") for (int q = 0; q < 4; q++) v += wv[ht][q] * relu(acc[ht][q]);       \
-      v = group4_sum(v);                                                                              \
-      if (grp == j) res = v;                                                                          \
+        _Pragma("unroll") for (int q = 0; q < 4; q++) v += wv[ht][q] * relu(acc[ht][q]);              \
+      vs[j] = v;                                                                                      \
     }                                                                                                 \
+    const float res = group4_transpose_sum(vs[0], vs[1], vs[2], vs[3]);                               \
     prev_key = (base) + grp * 16 + col;                                                               \
     prev_res = res;                                                                                   \
   }
