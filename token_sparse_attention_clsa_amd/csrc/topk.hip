@@ -15,18 +15,19 @@
 //      reaches about twice the rank k would have in the sample; the bin's
 //      lower bound is the threshold key. It then writes, in position order,
 //      the (position, key) pairs of its 4096-element chunk at or above the
-//      threshold (at most kTopkSegCap of them) and their count. With a 2048-element sample the chance that this
-//      keeps fewer than k positions, or more than the cap in a chunk, is
-//      negligible for any smooth score distribution, and the next kernel
-//      checks both anyway.
+//      threshold (at most kTopkSegCap of them) and their count. With a
+//      2048-element sample the chance that this keeps fewer than k
+//      positions, or more than the cap in a chunk, is negligible for any
+//      smooth score distribution, and the next kernel checks both anyway.
 //   2. topk_select (rows, 1024 threads): gathers the candidate segments (in
 //      chunk order, hence position order) into LDS and resolves the k-th key
 //      theta exactly with LDS histograms over the candidates' own key range
-//      (key - min, 12 bits per pass), then emits, in one ordered scan, keys
-//      above theta and the first `quota` keys equal to theta. If
-//      the candidates number fewer than k or a chunk overflowed its segment,
-//      it redoes the row on its own (LDS histogram of the full row, ordered
-//      candidate pass), so the result is exact whatever the sample did.
+//      (key - min, 12 bits per pass; a last bin of at most 64 keys is ranked
+//      by one wave), then emits, in one ordered scan, keys above theta and
+//      the first `quota` keys equal to theta. If the candidates number fewer
+//      than k or a chunk overflowed its segment, it redoes the row on its own
+//      (LDS histogram of the full row's top 12 bits, ordered candidate pass),
+//      so the result is exact whatever the sample did.
 // Rows whose visible count is <= k take every visible position. With a
 // per-row count k_rows[row] (clamped to [0, k]), a row keeps its k_rows[row]
 // best positions and the rest of its k slots hold -1.
@@ -35,7 +36,7 @@
 namespace clsa {
 namespace {
 
-constexpr int kBins0 = kTopkBins;  // top digit: 12 bits
+constexpr int kBins0 = kTopkBins;  // bins of a 12-bit digit
 constexpr int kThreads = 1024;     // topk_select
 constexpr int kWaves = kThreads / kWave;
 constexpr int kFilterThreads = 256;
