@@ -477,7 +477,8 @@ def main():
     if wl.T == 1:
         cold_gbs = alg["sparse_attn"] / (us_attn_cold * 1e-6) / 1e9
         attn_roof.update({"cold_achieved": cold_gbs, "cold_frac": cold_gbs / HBM_PEAK_GBS,
-                          "measured_copy_gbs": copy_gbs, "frac_of_measured_copy": attn_gbs / copy_gbs})
+                          "measured_copy_gbs": copy_gbs, "frac_of_measured_copy": attn_gbs / copy_gbs,
+                          "cold_frac_of_measured_copy": cold_gbs / copy_gbs})
     # The dominant kernel is the one with the larger share of the step: the
     # attention call (n layers) or the indexer (F layers). A chunk's indexer
     # is a contraction priced by its flops (2 * H_I * D_I per visible key);
