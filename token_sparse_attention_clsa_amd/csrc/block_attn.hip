@@ -65,6 +65,53 @@ typedef __attribute__((address_space(3))) void lds_void;
 __device__ __forceinline__ int k_chunk_at(int r, int c) { return r * kRowB + 16 * (c ^ (r & 7)); }
 __device__ __forceinline__ int v_chunk_at(int r, int c) { return r * kRowB + 16 * (c ^ (2 * (r & 3))); }
 
+// Online softmax of one column tile's 16 scores per lane (4 key tiles x 4),
+// the row spread over the 4 lanes that hold it: updates the running max m
+// and this lane's share l of the row sum, writes P as bf16 pairs in the slot
+// order of the PV k-steps and returns the rescale factor of the
+// accumulators. MASK: positions kp (this lane's 16 keys) outside [0, vis)
+// count as -inf. Without it (every key valid and visible; kp unused) the max
+// runs on the raw scores (the scale is positive) and exp2 takes
+// fma(s, scale, -max).
+template <bool MASK>
+__device__ __forceinline__ float tile_softmax(f32x4 (&sc)[4], const int (&kp)[4][4], int vis,
+                                              float c_log2, float& m, float& l, uint32_t (&pp)[8]) {
+  float mt_max = -INFINITY;
+#pragma unroll
+  for (int nt = 0; nt < 4; nt++)
+#pragma unroll
+    for (int r = 0; r < 4; r++) {
+      if constexpr (MASK) {
+        const int p = kp[nt][r];
+        sc[nt][r] = (p >= 0 && p < vis) ? sc[nt][r] * c_log2 : -INFINITY;
+      }
+      mt_max = fmaxf(mt_max, sc[nt][r]);
+    }
+  if constexpr (!MASK) mt_max *= c_log2;
+  mt_max = fmaxf(mt_max, __shfl_xor(mt_max, 16, kWave));
+  mt_max = fmaxf(mt_max, __shfl_xor(mt_max, 32, kWave));
+  const float mn = fmaxf(m, mt_max);
+  const float alpha = mn == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m - mn);
+  m = mn;
+  float psum = 0.f;
+#pragma unroll
+  for (int nt = 0; nt < 4; nt++) {
+    float p4[4];
+#pragma unroll
+    for (int r = 0; r < 4; r++) {
+      if constexpr (MASK)
+        p4[r] = sc[nt][r] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sc[nt][r] - mn);
+      else
+        p4[r] = __builtin_amdgcn_exp2f(fmaf(sc[nt][r], c_log2, -mn));
+      psum += p4[r];
+    }
+    pp[2 * nt] = pack_bf16(p4[0], p4[1]);
+    pp[2 * nt + 1] = pack_bf16(p4[2], p4[3]);
+  }
+  l = l * alpha + psum;
+  return alpha;
+}
+
 // grid (ceil(T / (kRows / G)), Hkv, B), block 512.
 template <int G>
 __global__ __launch_bounds__(kWaves * kWave) void block_attn_mfma(
@@ -105,6 +152,13 @@ __global__ __launch_bounds__(kWaves * kWave) void block_attn_mfma(
     for (int ks = 0; ks < 4; ks++)
       qf[c][ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(q + row[c] * kD + 8 * grp + 32 * ks));
   }
+
+  // Smallest visible length over the wave's rows (inactive rows see every
+  // key), uniform over the wave.
+  int vis_min = min(vis[0], vis[1]);
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) vis_min = min(vis_min, __shfl_xor(vis_min, off, kWave));
+  vis_min = __builtin_amdgcn_readfirstlane(vis_min);
 
   f32x4 o[2][8];  // O^T tiles: lane holds d = 16*mt + 4*grp + r of its row in tile c
 #pragma unroll
@@ -204,46 +258,26 @@ _Pragma("unroll")                                                               
       const int4 v4 = *reinterpret_cast<const int4*>(&(SP)[16 * nt + 4 * grp]);                                \
       kp[nt][0] = v4.x; kp[nt][1] = v4.y; kp[nt][2] = v4.z; kp[nt][3] = v4.w;                                  \
     }                                                                                                          \
-_Pragma("unroll")                                                                                              \
-    for (int c = 0; c < 2; c++) {                                                                              \
-      /* Mask, scale, running max over this lane's 16 keys, then the row's 4 lanes. */                         \
-      float mt_max = -INFINITY;                                                                                \
-_Pragma("unroll")                                                                                              \
-      for (int nt = 0; nt < 4; nt++)                                                                           \
-_Pragma("unroll")                                                                                              \
-        for (int r = 0; r < 4; r++) {                                                                          \
-          const int p = kp[nt][r];                                                                             \
-          const float x = (p >= 0 && p < vis[c]) ? s[c][nt][r] * c_log2 : -INFINITY;                           \
-          s[c][nt][r] = x;                                                                                     \
-          mt_max = fmaxf(mt_max, x);                                                                           \
-        }                                                                                                      \
-      mt_max = fmaxf(mt_max, __shfl_xor(mt_max, 16, kWave));                                                   \
-      mt_max = fmaxf(mt_max, __shfl_xor(mt_max, 32, kWave));                                                   \
-      const float mn = fmaxf(m[c], mt_max);                                                                    \
-      const float alpha = mn == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m[c] - mn);                           \
-      m[c] = mn;                                                                                               \
-      float psum = 0.f;                                                                                        \
-      uint32_t pp[8];  /* P as bf16 pairs, slot order of the PV k-steps */                                     \
-_Pragma("unroll")                                                                                              \
-      for (int nt = 0; nt < 4; nt++) {                                                                         \
-        float p4[4];                                                                                           \
-_Pragma("unroll")                                                                                              \
-        for (int r = 0; r < 4; r++) {                                                                          \
-          p4[r] = s[c][nt][r] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(s[c][nt][r] - mn);                   \
-          psum += p4[r];                                                                                       \
-        }                                                                                                      \
-        pp[2 * nt] = pack_bf16(p4[0], p4[1]);                                                                  \
-        pp[2 * nt + 1] = pack_bf16(p4[2], p4[3]);                                                              \
-      }                                                                                                        \
-      l[c] = l[c] * alpha + psum;                                                                              \
-      if (__ballot(alpha != 1.f) != 0) {  /* some row's max moved: rescale */                                  \
-_Pragma("unroll")                                                                                              \
-        for (int mt = 0; mt < 8; mt++) o[c][mt] *= alpha;                                                      \
-      }                                                                                                        \
-_Pragma("unroll")                                                                                              \
-      for (int ks = 0; ks < 2; ks++)                                                                           \
-        pf[c][ks] = __builtin_bit_cast(bf16x8, uint4{pp[4 * ks], pp[4 * ks + 1], pp[4 * ks + 2], pp[4 * ks + 3]}); \
-    }                                                                                                          \
+    /* A tile whose positions are all valid and visible to every row of the wave (its positions               \
+       ascend, so its first and last decide) takes the unmasked softmax. */                                   \
+    const int p_first = __builtin_amdgcn_readfirstlane((SP)[0]);                                              \
+    const int p_last = __builtin_amdgcn_readfirstlane((SP)[kKT - 1]);                                         \
+_Pragma("unroll")                                                                                             \
+    for (int c = 0; c < 2; c++) {                                                                             \
+      uint32_t pp[8];  /* P as bf16 pairs, slot order of the PV k-steps */                                    \
+      float alpha;                                                                                            \
+      if (p_first >= 0 && p_last >= 0 && p_last < vis_min)                                                    \
+        alpha = tile_softmax<false>(s[c], kp, vis[c], c_log2, m[c], l[c], pp);                                \
+      else                                                                                                    \
+        alpha = tile_softmax<true>(s[c], kp, vis[c], c_log2, m[c], l[c], pp);                                 \
+      if (__ballot(alpha != 1.f) != 0) {  /* some row's max moved: rescale */                                 \
+_Pragma("unroll")                                                                                             \
+        for (int mt = 0; mt < 8; mt++) o[c][mt] *= alpha;                                                     \
+      }                                                                                                       \
+_Pragma("unroll")                                                                                             \
+      for (int ks = 0; ks < 2; ks++)                                                                          \
+        pf[c][ks] = __builtin_bit_cast(bf16x8, uint4{pp[4 * ks], pp[4 * ks + 1], pp[4 * ks + 2], pp[4 * ks + 3]});\
+    }                                                                                                         \
     /* O^T += V^T P^T over 2 k-steps of 32 keys, both column tiles per V^T */                                  \
     /* fragment. Lane (grp, i) names V[4*grp + i/4 + 32*ks + 16*h][16*mt + 4*(i%4)]. */                        \
     const int vkey = 4 * grp + col / 4, vd4 = 4 * (col % 4);                                                   \
