@@ -88,8 +88,12 @@ __device__ __forceinline__ float tile_softmax(f32x4 (&sc)[4], const int (&kp)[4]
       mt_max = fmaxf(mt_max, sc[nt][r]);
     }
   if constexpr (!MASK) mt_max *= c_log2;
-  mt_max = fmaxf(mt_max, __shfl_xor(mt_max, 16, kWave));
-  mt_max = fmaxf(mt_max, __shfl_xor(mt_max, 32, kWave));
+  {  // max over the row's 4 lanes (l, l^16, l^32, l^48) by lane swaps
+    const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(mt_max), __float_as_uint(mt_max), false, false);
+    mt_max = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(mt_max), __float_as_uint(mt_max), false, false);
+    mt_max = fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+  }
   const float mn = fmaxf(m, mt_max);
   const float alpha = mn == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m - mn);
   m = mn;
