@@ -374,31 +374,9 @@ __device__ int histogram_and_candidates(const float* srow, int vis, int k, uint3
   return total;
 }
 
-// grid (nchunks, rows), block 256.
-__global__ __launch_bounds__(kFilterThreads) void topk_filter(const float* __restrict__ scores,
-                                                              uint32_t* __restrict__ counts,
-                                                              int2* __restrict__ cand, int T,
-                                                              int kv_len, int k,
-                                                              const int32_t* __restrict__ k_rows,
-                                                              int nchunks) {
-  __shared__ __attribute__((aligned(16))) uint32_t h[kBins0];
-  __shared__ int tmp[17];
-  __shared__ int res[3];
-  __shared__ uint32_t fmm[2][kFilterThreads / kWave];
-  const int row = blockIdx.y;
-  const int vis = kv_len - T + (row % T) + 1;
-  const int c0 = blockIdx.x * kChunk;
-  uint32_t* cnt = counts + (size_t)row * nchunks + blockIdx.x;
-  if (k_rows) k = min(max(k_rows[row], 0), k);
-  if (vis <= k || c0 >= vis || k == 0) {
-    if (threadIdx.x == 0) *cnt = 0u;
-    return;
-  }
-  const float* srow = scores + (size_t)row * kv_len;
-  // This thread's 16 chunk elements are loaded first, so that their memory
-  // latency overlaps the sample's.
+// This thread's 16 consecutive elements of the chunk at c0 as keys (0 past vis).
+__device__ __forceinline__ void load_chunk_keys(const float* srow, int c0, int vis, uint32_t (&key)[16]) {
   const int e0 = c0 + threadIdx.x * 16;
-  uint32_t key[16];
   if (e0 + 15 < vis && (reinterpret_cast<uintptr_t>(srow + e0) & 15) == 0) {
     const float4* p4 = reinterpret_cast<const float4*>(srow + e0);
     float4 v[4] = {p4[0], p4[1], p4[2], p4[3]};
@@ -409,6 +387,34 @@ __global__ __launch_bounds__(kFilterThreads) void topk_filter(const float* __res
 #pragma unroll
     for (int j = 0; j < 16; j++) key[j] = e0 + j < vis ? score_key(srow[e0 + j]) : 0u;
   }
+}
+
+// grid (ceil(nchunks / cpw), rows), block 256: a workgroup takes cpw
+// consecutive chunks of its row (one threshold for all of them).
+__global__ __launch_bounds__(kFilterThreads) void topk_filter(const float* __restrict__ scores,
+                                                              uint32_t* __restrict__ counts,
+                                                              int2* __restrict__ cand, int T,
+                                                              int kv_len, int k,
+                                                              const int32_t* __restrict__ k_rows,
+                                                              int nchunks, int cpw) {
+  __shared__ __attribute__((aligned(16))) uint32_t h[kBins0];
+  __shared__ int tmp[17];
+  __shared__ int res[3];
+  __shared__ uint32_t fmm[2][kFilterThreads / kWave];
+  const int row = blockIdx.y;
+  const int vis = kv_len - T + (row % T) + 1;
+  const int ci0 = blockIdx.x * cpw, ci1 = min(nchunks, ci0 + cpw);
+  uint32_t* cnt = counts + (size_t)row * nchunks;
+  if (k_rows) k = min(max(k_rows[row], 0), k);
+  if (vis <= k || ci0 * kChunk >= vis || k == 0) {
+    for (int ci = ci0 + threadIdx.x; ci < ci1; ci += blockDim.x) cnt[ci] = 0u;
+    return;
+  }
+  const float* srow = scores + (size_t)row * kv_len;
+  // The first chunk's elements are loaded first, so that their memory
+  // latency overlaps the sample's.
+  uint32_t key[16];
+  load_chunk_keys(srow, ci0 * kChunk, vis, key);
   // Threshold from the row's sample (identical in every workgroup): the
   // whole row when it is short, else kSample / kSampleRun runs of kSampleRun
   // consecutive elements, the first at 0 and the last ending at vis - 1. The
@@ -463,26 +469,35 @@ __global__ __launch_bounds__(kFilterThreads) void topk_filter(const float* __res
   const int r = (int)min((long)m, 2 * expect + 8);
   find_bin(h, nb, r, res, tmp);
   const uint32_t thr = mn + ((uint32_t)res[0] << sh);
-  // Ordered compaction of this chunk's positions whose key is >= thr.
-  uint32_t flags = 0;
-  int c = 0;
-#pragma unroll
-  for (int j = 0; j < 16; j++) {
-    if (e0 + j < vis && key[j] >= thr) {
-      flags |= 1u << j;
-      c++;
+  // Ordered compaction of each chunk's positions whose key is >= thr.
+  for (int ci = ci0; ci < ci1; ci++) {  // uniform over the workgroup
+    const int c0 = ci * kChunk;
+    if (c0 >= vis) {
+      if (threadIdx.x == 0) cnt[ci] = 0u;
+      continue;
     }
+    if (ci != ci0) load_chunk_keys(srow, c0, vis, key);
+    const int e0 = c0 + threadIdx.x * 16;
+    uint32_t flags = 0;
+    int c = 0;
+#pragma unroll
+    for (int j = 0; j < 16; j++) {
+      if (e0 + j < vis && key[j] >= thr) {
+        flags |= 1u << j;
+        c++;
+      }
+    }
+    int total;
+    int o = block_exclusive_scan(c, tmp, &total);
+    int2* seg = cand + ((size_t)row * nchunks + ci) * kTopkSegCap;
+#pragma unroll
+    for (int j = 0; j < 16; j++)
+      if (flags >> j & 1u) {
+        if (o < kTopkSegCap) seg[o] = make_int2(e0 + j, (int)key[j]);
+        o++;
+      }
+    if (threadIdx.x == 0) cnt[ci] = (uint32_t)total;  // above kTopkSegCap: the row is redone
   }
-  int total;
-  int o = block_exclusive_scan(c, tmp, &total);
-  int2* seg = cand + ((size_t)row * nchunks + blockIdx.x) * kTopkSegCap;
-#pragma unroll
-  for (int j = 0; j < 16; j++)
-    if (flags >> j & 1u) {
-      if (o < kTopkSegCap) seg[o] = make_int2(e0 + j, (int)key[j]);
-      o++;
-    }
-  if (threadIdx.x == 0) *cnt = (uint32_t)total;  // above kTopkSegCap: the row is redone
 }
 
 // grid (rows), block 1024.
@@ -618,8 +633,13 @@ int launch_topk(const float* scores, int B, int T, int kv_len, int k, const int3
   if (tb.nchunks > kTopkMaxChunks)
     return set_error(CLSA_ERR_UNSUPPORTED, "topk: kv_len=%d above %d", kv_len, kTopkMaxChunks * kChunk);
   int2* segs = reinterpret_cast<int2*>(cand);
-  hipLaunchKernelGGL(topk_filter, dim3(tb.nchunks, rows), dim3(kFilterThreads), 0, stream, scores,
-                     counts, segs, T, kv_len, k, k_rows, tb.nchunks);
+  // Chunks per filter workgroup: one while the grid stays small (decode),
+  // more when rows are many (a chunk's queries), so the row's threshold is
+  // computed once per cpw chunks; about 8192 workgroups at most.
+  const long total_chunks = (long)rows * tb.nchunks;
+  int cpw = (int)min((long)tb.nchunks, max(1L, total_chunks / 8192));
+  hipLaunchKernelGGL(topk_filter, dim3((tb.nchunks + cpw - 1) / cpw, rows), dim3(kFilterThreads), 0,
+                     stream, scores, counts, segs, T, kv_len, k, k_rows, tb.nchunks, cpw);
   int rc = check_launch("topk_filter");
   if (rc) return rc;
   hipLaunchKernelGGL(topk_select, dim3(rows), dim3(kThreads), 0, stream, scores, counts, segs, spill,
