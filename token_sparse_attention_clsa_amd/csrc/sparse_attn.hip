@@ -267,7 +267,7 @@ __global__ __launch_bounds__(kWave * kMaxWaves) void attn_split_kernel(
 // it needs straight from the query's index row. Lane l = 16 * grp + col.
 //  - Scores: S^T[key, h] = K[key, :] . q[h, :] with v_mfma_f32_16x16x32_bf16.
 //    A = 16 gathered K rows (lane: key col, d = 8 * grp + 32 * ks + 0..7),
-//    B = the G query heads (lane: head col, zero for col >= G). Lane
+//    B = the G query heads (lane: head col; columns >= G repeat head G - 1, unused). Lane
 //    (grp, col) receives head col for keys 4 * grp + r of each tile.
 //  - Softmax: one running max per head shared by the four lane groups (a
 //    cross-group max through v_permlane16/32_swap), so the per-group partial
@@ -457,13 +457,15 @@ __global__ __launch_bounds__(kWave * kMaxWaves) void attn_split_mfma(
     const char* __restrict__ q, const char* __restrict__ kc, const char* __restrict__ vc,
     const int32_t* __restrict__ idx, int k, void* __restrict__ out, float* __restrict__ lse,
     int T, int Hkv, int kv_len, int L_cap, float c_log2, int rows_per_split,
-    float* __restrict__ partials) {
+    float* __restrict__ partials, int gpw) {
+  // gpw: KV heads per workgroup (blockDim.x = 64 * W * gpw). It is an argument
+  // rather than derived from blockDim.x, whose read from the dispatch's hidden
+  // arguments is a vector load the whole prologue would wait for.
   constexpr int ROW = kD * 2;
   __shared__ __attribute__((aligned(16))) char s_vt[kMaxWaves * kVtBytes];
   __shared__ float s_ml[kMaxWaves][16][2];
   const int lane = threadIdx.x % kWave;
   const int wave = threadIdx.x / kWave;
-  const int gpw = blockDim.x / (kWave * W);  // KV heads per workgroup
   const int col = lane % 16;
   const int grp = lane / 16;
   const int split = blockIdx.x, S = gridDim.x;
@@ -479,13 +481,15 @@ __global__ __launch_bounds__(kWave * kMaxWaves) void attn_split_mfma(
   char* vt = s_vt + wave * kVtBytes;
 
   bf16x8 qf[4];
+  // B columns col >= G hold no head: they load head G - 1 again (their
+  // scores, softmax and outputs stay in their own columns and are never
+  // stored). An unconditional load keeps the q loads in flight with the
+  // index loads that follow instead of waiting for them first.
+  const int qh = g * G + min(col, G - 1);
 #pragma unroll
-  for (int ks = 0; ks < 4; ks++) {
-    uint4 u = {0u, 0u, 0u, 0u};
-    if (col < G)
-      u = *reinterpret_cast<const uint4*>(q + (((size_t)bt * Hq + g * G + col) * kD + 8 * grp + 32 * ks) * 2);
-    qf[ks] = __builtin_bit_cast(bf16x8, u);
-  }
+  for (int ks = 0; ks < 4; ks++)
+    qf[ks] = __builtin_bit_cast(
+        bf16x8, *reinterpret_cast<const uint4*>(q + (((size_t)bt * Hq + qh) * kD + 8 * grp + 32 * ks) * 2));
   MfmaState st;
 #pragma unroll
   for (int j = 0; j < 8; j++) st.o[j] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -652,12 +656,12 @@ int launch_index_path(const void* q, const void* kc, const void* vc, const int32
     hipLaunchKernelGGL((attn_split_mfma<G, W, true>), grid, block, 0, stream,                \
                        static_cast<const char*>(q), static_cast<const char*>(kc),            \
                        static_cast<const char*>(vc), idx, k, out, lse, T, Hkv, kv_len, L_cap, \
-                       c_log2, sp.rows_per_split, partials);                                 \
+                       c_log2, sp.rows_per_split, partials, gpw);                            \
   else                                                                                       \
   hipLaunchKernelGGL((attn_split_mfma<G, W, false>), grid, block, 0, stream,                 \
                      static_cast<const char*>(q), static_cast<const char*>(kc),              \
                      static_cast<const char*>(vc), idx, k, out, lse, T, Hkv, kv_len, L_cap,  \
-                     c_log2, sp.rows_per_split, partials)
+                     c_log2, sp.rows_per_split, partials, gpw)
     if (sp.waves_per_head == 4) CLSA_SPLIT_MFMA(4);
     else if (sp.waves_per_head == 2) CLSA_SPLIT_MFMA(2);
     else CLSA_SPLIT_MFMA(1);
