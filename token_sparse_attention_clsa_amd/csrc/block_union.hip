@@ -49,16 +49,16 @@ __global__ __launch_bounds__(kCompactThreads) void union_compact(const uint32_t*
     const uint32_t* f = flags + (size_t)b * nblk;
     // Pass 1: number of flagged blocks of this batch element.
     int cnt = 0;
-    for (int i = threadIdx.x; i < nblk; i += blockDim.x) cnt += f[i] != 0u;
+    for (int i = threadIdx.x; i < nblk; i += kCompactThreads) cnt += f[i] != 0u;
     int nb;
-    block_exclusive_scan(cnt, tmp, &nb);
+    block_exclusive_scan<kCompactThreads>(cnt, tmp, &nb);
     // Pass 2: ordered write, once per KV group.
     int run = 0;
-    for (int t0 = 0; t0 < nblk; t0 += blockDim.x) {
+    for (int t0 = 0; t0 < nblk; t0 += kCompactThreads) {
       const int i = t0 + threadIdx.x;
       const int flag = (i < nblk && f[i] != 0u) ? 1 : 0;
       int tot;
-      const int off = run + block_exclusive_scan(flag, tmp, &tot);
+      const int off = run + block_exclusive_scan<kCompactThreads>(flag, tmp, &tot);
       if (flag)
         for (int g = 0; g < Hkv; g++) indices[base + g * nb + off] = i;
       run += tot;

@@ -69,15 +69,19 @@ __device__ __forceinline__ T wave_sum(T v) {
   return v;
 }
 
-// Exclusive scan of one int per thread over the whole block (blockDim.x a
-// multiple of 64, at most 1024). `tmp` is __shared__ int[16 + 1] (the first
-// blockDim.x / 64 entries are used). Returns the thread's exclusive prefix;
-// *total receives the block total. Contains barriers: every thread of the
-// block must call it, with the whole wave active.
+// Exclusive scan of one int per thread over the whole block of NT threads
+// (the launch's block size: a multiple of 64, at most 1024; a compile-time
+// constant, since reading blockDim.x costs a load from the dispatch's hidden
+// arguments). `tmp` is __shared__ int[16 + 1] (the first NT / 64 entries are
+// used). Returns the thread's exclusive prefix; *total receives the block
+// total. Contains barriers: every thread of the block must call it, with the
+// whole wave active.
+template <int NT>
 __device__ __forceinline__ int block_exclusive_scan(int v, int* tmp, int* total) {
+  static_assert(NT % kWave == 0 && NT <= 1024, "block size");
   const int lane = lane_id();
   const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-  const int nw = blockDim.x / kWave;
+  constexpr int nw = NT / kWave;
   const int inc = wave_inclusive_scan(v);
   if (lane == kWave - 1) tmp[wid] = inc;
   __syncthreads();

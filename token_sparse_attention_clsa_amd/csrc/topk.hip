@@ -54,16 +54,17 @@ constexpr int kHistCopies = 2;     // fallback histogram copies
 // totals through tmp and one barrier give each thread the count above its
 // bins, and the thread where `need` falls walks them; res[2] = the count in
 // bin b. Every thread of the block must call it; need must be in [1, total];
-// tmp is int[16].
+// tmp is int[16]; NT = the block size.
+template <int NT>
 __device__ void find_bin(const uint32_t* h, int nbins, int need, int* res, int* tmp) {
-  const int per = (nbins + blockDim.x - 1) / blockDim.x;
+  const int per = (nbins + NT - 1) / NT;
   const int hi = nbins - 1 - (int)threadIdx.x * per;
   int sum = 0;
   for (int j = 0; j < per; j++)
     if (hi - j >= 0) sum += h[hi - j];
   const int lane = threadIdx.x % kWave;
   const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-  const int nw = blockDim.x / kWave;
+  constexpr int nw = NT / kWave;
   const int inc = wave_inclusive_scan(sum);
   if (lane == kWave - 1) tmp[wid] = inc;
   __syncthreads();
@@ -151,15 +152,15 @@ __device__ void select_and_emit(const Acc& acc, int n, int need, uint32_t lo, ui
     const int bits = 63 - __clzll(R);
     const int s = bits > 12 ? bits - 12 : 0;
     const int nb = (int)(R >> s);
-    for (int i = threadIdx.x; i < nb; i += blockDim.x) h[i] = 0u;
+    for (int i = threadIdx.x; i < nb; i += kThreads) h[i] = 0u;
     if (threadIdx.x == 0) nfew = 0;
     __syncthreads();
-    for (int i = threadIdx.x; i < n; i += blockDim.x) {
+    for (int i = threadIdx.x; i < n; i += kThreads) {
       const uint32_t key = acc.k(i);
       if (key >= lo && (uint64_t)(key - lo) < R) atomicAdd(&h[(key - lo) >> s], 1u);
     }
     __syncthreads();
-    find_bin(h, nb, need, res, tmp);
+    find_bin<kThreads>(h, nb, need, res, tmp);
     // Every thread reads res here, before the next pass's first barrier;
     // it is rewritten only after that pass's third one.
     lo += (uint32_t)res[0] << s;
@@ -169,7 +170,7 @@ __device__ void select_and_emit(const Acc& acc, int n, int need, uint32_t lo, ui
       // At most 64 keys left in [lo, lo + R): one wave ranks them (keys
       // strictly above and equal to each) instead of further passes.
       const int cnt = res[2];
-      for (int i = threadIdx.x; i < n; i += blockDim.x) {
+      for (int i = threadIdx.x; i < n; i += kThreads) {
         const uint32_t key = acc.k(i);
         if (key >= lo && (uint64_t)(key - lo) < R) few[atomicAdd(&nfew, 1)] = key;
       }
@@ -198,11 +199,11 @@ __device__ void select_and_emit(const Acc& acc, int n, int need, uint32_t lo, ui
   const uint32_t theta = lo;
   const int quota = need;  // how many keys equal to theta are taken
   // Ordered emission: thread t owns the run [t0 + t * run, t0 + (t + 1) * run)
-  // of the tile (run <= 16), so up to 16 * blockDim.x candidates take one
+  // of the tile (run <= 16), so up to 16 * kThreads candidates take one
   // block scan and no barrier waits behind the output stores.
-  const int run = min(16, max(1, (n + (int)blockDim.x - 1) / (int)blockDim.x));
+  const int run = min(16, max(1, (n + kThreads - 1) / kThreads));
   int gt_base = 0, eq_base = 0;
-  for (int t0 = 0; t0 < n; t0 += run * blockDim.x) {  // uniform over the workgroup
+  for (int t0 = 0; t0 < n; t0 += run * kThreads) {  // uniform over the workgroup
     const int i0 = t0 + threadIdx.x * run;
     int gt = 0, eq = 0;
     for (int e = 0; e < run; e++) {
@@ -213,7 +214,7 @@ __device__ void select_and_emit(const Acc& acc, int n, int need, uint32_t lo, ui
       }
     }
     int tot;  // per tile both counts stay below 2^16
-    const int pre_cnt = block_exclusive_scan((eq << 16) | gt, tmp, &tot);
+    const int pre_cnt = block_exclusive_scan<kThreads>((eq << 16) | gt, tmp, &tot);
     int g = gt_base + (pre_cnt & 0xffff);
     int q = eq_base + (pre_cnt >> 16);
     for (int e = 0; e < run; e++) {
@@ -252,7 +253,8 @@ __device__ void select_top(const Acc& acc, int n, int k, uint32_t mn, uint32_t m
 __device__ void block_minmax(uint32_t& mn, uint32_t& mx, uint32_t (*mm)[kWaves]) {
   mn = wave_min_u32(mn);
   mx = wave_max_u32(mx);
-  const int wave = threadIdx.x / kWave, nw = blockDim.x / kWave;
+  const int wave = threadIdx.x / kWave;
+  constexpr int nw = kWaves;
   if (threadIdx.x % kWave == 0) {
     mm[0][wave] = mn;
     mm[1][wave] = mx;
@@ -306,7 +308,7 @@ __device__ int histogram_and_candidates(const float* srow, int vis, int k, uint3
     h[i] = c;
   }
   __syncthreads();
-  find_bin(h, kBins0, k, res, tmp);
+  find_bin<kThreads>(h, kBins0, k, res, tmp);
   const uint32_t b0 = (uint32_t)res[0];
   *b0_out = b0;
   *above_out = res[1];
@@ -407,7 +409,7 @@ __global__ __launch_bounds__(kFilterThreads) void topk_filter(const float* __res
   uint32_t* cnt = counts + (size_t)row * nchunks;
   if (k_rows) k = min(max(k_rows[row], 0), k);
   if (vis <= k || ci0 * kChunk >= vis || k == 0) {
-    for (int ci = ci0 + threadIdx.x; ci < ci1; ci += blockDim.x) cnt[ci] = 0u;
+    for (int ci = ci0 + threadIdx.x; ci < ci1; ci += kFilterThreads) cnt[ci] = 0u;
     return;
   }
   const float* srow = scores + (size_t)row * kv_len;
@@ -450,7 +452,7 @@ __global__ __launch_bounds__(kFilterThreads) void topk_filter(const float* __res
     fmm[0][wave] = mn;
     fmm[1][wave] = mx;
   }
-  for (int i = threadIdx.x; i < kBins0; i += blockDim.x) h[i] = 0u;
+  for (int i = threadIdx.x; i < kBins0; i += kFilterThreads) h[i] = 0u;
   __syncthreads();
 #pragma unroll
   for (int w = 0; w < kFilterThreads / kWave; w++) {
@@ -467,7 +469,7 @@ __global__ __launch_bounds__(kFilterThreads) void topk_filter(const float* __res
   __syncthreads();
   const long expect = ((long)k * m + vis - 1) / vis;  // rank of the k-th key in the sample
   const int r = (int)min((long)m, 2 * expect + 8);
-  find_bin(h, nb, r, res, tmp);
+  find_bin<kFilterThreads>(h, nb, r, res, tmp);
   const uint32_t thr = mn + ((uint32_t)res[0] << sh);
   // Ordered compaction of each chunk's positions whose key is >= thr.
   for (int ci = ci0; ci < ci1; ci++) {  // uniform over the workgroup
@@ -488,7 +490,7 @@ __global__ __launch_bounds__(kFilterThreads) void topk_filter(const float* __res
       }
     }
     int total;
-    int o = block_exclusive_scan(c, tmp, &total);
+    int o = block_exclusive_scan<kFilterThreads>(c, tmp, &total);
     int2* seg = cand + ((size_t)row * nchunks + ci) * kTopkSegCap;
 #pragma unroll
     for (int j = 0; j < 16; j++)
@@ -552,7 +554,7 @@ __global__ __launch_bounds__(kThreads) void topk_select(const float* __restrict_
   {
     const int c = threadIdx.x;
     const int v = c < nchunks ? (int)counts[(size_t)row * nchunks + c] : 0;
-    const int o = block_exclusive_scan(v, tmp, &n);
+    const int o = block_exclusive_scan<kThreads>(v, tmp, &n);
     if (c < nchunks) off[c] = o;
     if (c == 0) off[nchunks] = n;
     overflow = __syncthreads_or(v > kTopkSegCap) != 0;
@@ -584,7 +586,7 @@ __global__ __launch_bounds__(kThreads) void topk_select(const float* __restrict_
       select_top(Cand{lpos, lkey, nullptr, srow}, n, k, mn, mx, h, res, tmp, out);
     } else {
       const SegCand acc{segs, off, nchunks};
-      for (int i = threadIdx.x; i < n; i += blockDim.x) {
+      for (int i = threadIdx.x; i < n; i += kThreads) {
         const uint32_t key = acc.k(i);
         mn = min(mn, key);
         mx = max(mx, key);
