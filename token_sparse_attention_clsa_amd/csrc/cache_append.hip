@@ -11,8 +11,11 @@
 namespace clsa {
 namespace {
 
-// grid (B*T rows, n jobs), block 256: workgroup (r, j) copies row r of job j.
-__global__ __launch_bounds__(256) void append_rows(AppendJob j0, AppendJob j1, AppendJob j2, int T,
+constexpr int kAppendThreads = 256;
+
+// grid (B*T rows, n jobs), block kAppendThreads: workgroup (r, j) copies row
+// r of job j.
+__global__ __launch_bounds__(kAppendThreads) void append_rows(AppendJob j0, AppendJob j1, AppendJob j2, int T,
                                                    int pos, int L_cap) {
   const AppendJob& j = blockIdx.y == 0 ? j0 : (blockIdx.y == 1 ? j1 : j2);
   const size_t r = blockIdx.x;
@@ -20,10 +23,10 @@ __global__ __launch_bounds__(256) void append_rows(AppendJob j0, AppendJob j1, A
   const char* src = j.src + r * j.row_bytes;
   char* dst = j.dst + (b * L_cap + pos + t) * j.row_bytes;
   if (j.row_bytes % 16 == 0) {  // 16-byte aligned rows: one uint4 per thread per pass
-    for (size_t i = threadIdx.x * 16; i < j.row_bytes; i += blockDim.x * 16)
+    for (size_t i = threadIdx.x * 16; i < j.row_bytes; i += kAppendThreads * 16)
       *reinterpret_cast<uint4*>(dst + i) = *reinterpret_cast<const uint4*>(src + i);
   } else {
-    for (size_t i = threadIdx.x; i < j.row_bytes; i += blockDim.x) dst[i] = src[i];
+    for (size_t i = threadIdx.x; i < j.row_bytes; i += kAppendThreads) dst[i] = src[i];
   }
 }
 
@@ -32,7 +35,7 @@ __global__ __launch_bounds__(256) void append_rows(AppendJob j0, AppendJob j1, A
 int launch_cache_append(const AppendJob* jobs, int n_jobs, int B, int T, int pos, int L_cap,
                         hipStream_t stream) {
   const AppendJob none{nullptr, nullptr, 0};
-  hipLaunchKernelGGL(append_rows, dim3((unsigned)((size_t)B * T), (unsigned)n_jobs), dim3(256), 0,
+  hipLaunchKernelGGL(append_rows, dim3((unsigned)((size_t)B * T), (unsigned)n_jobs), dim3(kAppendThreads), 0,
                      stream, jobs[0], n_jobs > 1 ? jobs[1] : none, n_jobs > 2 ? jobs[2] : none, T,
                      pos, L_cap);
   return check_launch("append_rows");

@@ -282,7 +282,8 @@ __global__ __launch_bounds__(kQB * kWave) void idx_score_multi(
 // Float32 indexer (small head counts): one thread per key, the query's heads
 // and weights staged in LDS. grid: (ceil(kv_len/256), B*T), block 256,
 // dynamic LDS (H*D + H) floats.
-__global__ __launch_bounds__(256) void idx_score_f32(const float* __restrict__ q_idx,
+constexpr int kF32Threads = 256;
+__global__ __launch_bounds__(kF32Threads) void idx_score_f32(const float* __restrict__ q_idx,
                                                      const float* __restrict__ k_idx,
                                                      const float* __restrict__ w,
                                                      float* __restrict__ scores, int T, int H,
@@ -291,10 +292,10 @@ __global__ __launch_bounds__(256) void idx_score_f32(const float* __restrict__ q
   const int bt = blockIdx.y;
   const int b = bt / T, t = bt % T;
   const int vis = kv_len - T + t + 1;
-  for (int i = threadIdx.x; i < H * D; i += blockDim.x) sh[i] = q_idx[(size_t)bt * H * D + i];
-  for (int i = threadIdx.x; i < H; i += blockDim.x) sh[H * D + i] = w[(size_t)bt * H + i];
+  for (int i = threadIdx.x; i < H * D; i += kF32Threads) sh[i] = q_idx[(size_t)bt * H * D + i];
+  for (int i = threadIdx.x; i < H; i += kF32Threads) sh[H * D + i] = w[(size_t)bt * H + i];
   __syncthreads();
-  const int s = blockIdx.x * blockDim.x + threadIdx.x;
+  const int s = blockIdx.x * kF32Threads + threadIdx.x;
   if (s >= kv_len) return;
   float* out = scores + (size_t)bt * kv_len + s;
   if (s >= vis) {
@@ -371,9 +372,9 @@ int launch_index_score(const void* q_idx, const void* k_idx, int idx_dtype, cons
                        float* scores, int B, int T, int H_I, int D_I, int kv_len, int L_cap,
                        hipStream_t stream) {
   if (idx_dtype == CLSA_F32) {
-    dim3 grid((kv_len + 255) / 256, B * T);
+    dim3 grid((kv_len + kF32Threads - 1) / kF32Threads, B * T);
     size_t lds = sizeof(float) * ((size_t)H_I * D_I + H_I);
-    hipLaunchKernelGGL(idx_score_f32, grid, dim3(256), lds, stream,
+    hipLaunchKernelGGL(idx_score_f32, grid, dim3(kF32Threads), lds, stream,
                        static_cast<const float*>(q_idx), static_cast<const float*>(k_idx), w,
                        scores, T, H_I, D_I, kv_len, L_cap);
     return check_launch("idx_score_f32");

@@ -168,14 +168,14 @@ __global__ __launch_bounds__(kWave * kMaxWaves) void attn_split_kernel(
     const char* __restrict__ q, const char* __restrict__ kc, const char* __restrict__ vc,
     const int32_t* __restrict__ idx, int k, void* __restrict__ out, float* __restrict__ lse,
     int T, int Hkv, int kv_len, int L_cap, float c_log2, int rows_per_split,
-    float* __restrict__ partials) {
+    float* __restrict__ partials, int nw) {
+  // nw: waves (KV heads) per workgroup, passed rather than read from blockDim.x.
   using E = AttnElem<DT>;
   constexpr int RPI = G <= 4 ? E::rows_per_step : 4;  // fewer rows in flight for 8 heads
   constexpr int ROW = kD * E::bytes;
   __shared__ int s_pos[kTileRows];
   const int lane = threadIdx.x % kWave;
   const int wave = threadIdx.x / kWave;
-  const int nw = blockDim.x / kWave;
   const int sub = lane % 16;  // element slice [8*sub, 8*sub + 8)
   const int rg = lane / 16;   // lane group: its own rows
   const int split = blockIdx.x, S = gridDim.x;
@@ -202,7 +202,7 @@ __global__ __launch_bounds__(kWave * kMaxWaves) void attn_split_kernel(
   for (int t0 = r0; t0 < r1; t0 += kTileRows) {  // uniform over the workgroup
     const int n = min(kTileRows, r1 - t0);
     __syncthreads();  // the previous tile's positions are no longer read
-    for (int i = threadIdx.x; i < n; i += blockDim.x) {
+    for (int i = threadIdx.x; i < n; i += nw * kWave) {
       const int p = irow[t0 + i];
       s_pos[i] = (p >= 0 && p < vis) ? p : -1;
     }
@@ -670,7 +670,7 @@ int launch_index_path(const void* q, const void* kc, const void* vc, const int32
     hipLaunchKernelGGL((attn_split_kernel<DT, G>), grid, block, 0, stream,
                        static_cast<const char*>(q), static_cast<const char*>(kc),
                        static_cast<const char*>(vc), idx, k, out, lse, T, Hkv, kv_len, L_cap,
-                       c_log2, sp.rows_per_split, partials);
+                       c_log2, sp.rows_per_split, partials, gpw);
   }
   int rc = check_launch("attn_split");
   if (rc || sp.splits == 1) return rc;
