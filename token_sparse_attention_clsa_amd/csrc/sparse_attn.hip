@@ -322,30 +322,46 @@ struct KvStep {
   uint32_t valid;  // bit 4 * tile + r: key 16 * tile + 4 * grp + r is visible
 };
 
-// Issues the loads of the step at index entries [e0, e0 + 32) of the
-// query's row. Each lane reads the positions it needs straight from the
-// index row (the 32 entries share one or two cache lines); entries at or
-// past `end`, negative, or outside the visible range are masked and read
-// cache row 0.
-__device__ __forceinline__ int vis_pos(const int32_t* irow, int e, int end, int vis) {
-  const int p = e < end ? irow[e] : -1;
-  return (p >= 0 && p < vis) ? p : -1;
+// This lane's raw index entries of one 32-entry step (entries e0 .. e0 + 31
+// of the query's row): the K row entry of each 16-key tile and the 4 V row
+// entries of its lane group in each tile. Every load is unconditional
+// (entries past `end` read entry end - 1; end >= 1) and the values are
+// masked only when the step is issued.
+struct IdxStep {
+  int k[2];
+  int v[2][4];
+};
+__device__ __forceinline__ void idx_fetch(IdxStep& x, const int32_t* irow, int e0, int end, int col,
+                                          int grp) {
+#pragma unroll
+  for (int tt = 0; tt < 2; tt++) {
+    x.k[tt] = irow[min(e0 + 16 * tt + col, end - 1)];
+#pragma unroll
+    for (int r = 0; r < 4; r++) x.v[tt][r] = irow[min(e0 + 16 * tt + 4 * grp + r, end - 1)];
+  }
 }
-// With SKIP, returns false and issues no load when none of the 32 entries
-// is visible (e.g. the -1 tail of a query that keeps fewer than k
+// Entry e with raw position p: the position if e is before `end` and p is
+// visible, else -1 (masked; its loads read cache row 0).
+__device__ __forceinline__ int vis_pos(int p, int e, int end, int vis) {
+  return (e < end && p >= 0 && p < vis) ? p : -1;
+}
+
+// Issues the K/V loads of the step at entries [e0, e0 + 32) from its index
+// entries x. With SKIP, returns false and issues no load when none of the 32
+// entries is visible (e.g. the -1 tail of a query that keeps fewer than k
 // positions); the result is uniform over the wave. Without SKIP the step is
 // always loaded (masked entries read row 0), which keeps the fixed-k code
 // free of the branch.
 template <bool SKIP>
-__device__ __forceinline__ bool kv_issue(KvStep& f, const int32_t* irow, int e0, int end, int vis,
+__device__ __forceinline__ bool kv_issue(KvStep& f, const IdxStep& x, int e0, int end, int vis,
                                          int col, int grp, const char* kb, const char* vb,
                                          size_t tok) {
   int kp[2], vp[2][4];
 #pragma unroll
   for (int tt = 0; tt < 2; tt++) {
-    kp[tt] = vis_pos(irow, e0 + 16 * tt + col, end, vis);
+    kp[tt] = vis_pos(x.k[tt], e0 + 16 * tt + col, end, vis);
 #pragma unroll
-    for (int r = 0; r < 4; r++) vp[tt][r] = vis_pos(irow, e0 + 16 * tt + 4 * grp + r, end, vis);
+    for (int r = 0; r < 4; r++) vp[tt][r] = vis_pos(x.v[tt][r], e0 + 16 * tt + 4 * grp + r, end, vis);
   }
   f.valid = 0u;
 #pragma unroll
@@ -480,6 +496,8 @@ __global__ __launch_bounds__(kWave * kMaxWaves) void attn_split_mfma(
   const int32_t* irow = idx + (size_t)bt * k;
   char* vt = s_vt + wave * kVtBytes;
 
+  IdxStep xi;  // the wave's first step, requested first: the gather waits on it
+  idx_fetch(xi, irow, r0 + 32 * w, r1, col, grp);
   bf16x8 qf[4];
   // B columns col >= G hold no head: they load head G - 1 again (their
   // scores, softmax and outputs stay in their own columns and are never
@@ -507,10 +525,15 @@ __global__ __launch_bounds__(kWave * kMaxWaves) void attn_split_mfma(
 
   // One 32-entry step at a time: at the usual split sizes a wave has one
   // or two steps, and the other waves of the SIMD cover its load latency.
+  // The first step's index entries were requested before the q loads; each
+  // later step's are requested once the previous step is consumed
+  // (prefetching them a step ahead measured slower on the 2K-query prefill,
+  // where a wave runs 128 steps).
   for (int e0 = r0 + 32 * w; e0 < r1; e0 += 32 * W) {  // uniform over the wave
     KvStep f;
-    if (kv_issue<SKIP>(f, irow, e0, r1, vis, col, grp, kb, vb, tok))
+    if (kv_issue<SKIP>(f, xi, e0, r1, vis, col, grp, kb, vb, tok))
       kv_consume(f, st, qf, vt, wbase, rbase, c_log2);
+    idx_fetch(xi, irow, e0 + 32 * W, r1, col, grp);
   }
   float l = xgroup_sum(st.l);
   float m = st.m;
