@@ -18,4 +18,5 @@ from .oracle import (  # noqa: F401
     index_score,
     sparse_attn,
     topk,
+    topk_margin,
 )

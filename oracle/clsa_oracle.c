@@ -21,6 +21,9 @@
  *          "2. Méthodologie : IndexCache".
  *  [CA]    gist.science summary of "CompactAttention: Accelerating Chunked
  *          Prefill with Block-Union KV Selection", section "Méthodologie".
+ *  [CoSA]  gist.science summary of "CoSA: Accelerating Long-Context Inference
+ *          via Proxy-Kernel Co-Designed Sparse Attention" (no section titles;
+ *          cited by the paragraphs on its proxy and its kernel).
  *
  * Readings of points the pages leave open (each is listed with its reason
  * in the design notes of the repository):
@@ -30,6 +33,8 @@
  *  - Causality: query t of a T-query call sees positions [0, kv_len - T + t].
  *  - Top-k order: score descending, then position ascending (lower position
  *    wins ties); chosen positions are returned ascending, padded with -1.
+ *  - Ordered skipping: the priority list is the top-k in that order; reading
+ *    stops at the first entry more than a fixed margin below the first one.
  *  - Attention uses one index per (b, t), shared by every head; softmax
  *    scale defaults to 1/sqrt(D); GQA groups are contiguous.
  *
@@ -233,10 +238,22 @@ static int orc_cmp_long(const void* a, const void* b) {
  * k_bt = k, or with k_rows [B,T] (the per-query count of the query-dependent
  * k reading; [CLSA] "Le coût : limites de compatibilité") k_rows[b,t]
  * clamped to [0, k].
+ *
+ * Ordered skipping ([CoSA] summary, the paragraphs on the Kernel-Aware Proxy
+ * and the Ordered-Skipping Kernel: the proxy hands over a priority list, the
+ * kernel reads the most important entries first and skips the rest). With
+ * margin != NULL the list above, in priority order, is read from its first
+ * entry and reading stops at the first entry whose score is below
+ * thr = s_first - *margin; only the entries read are kept. The pages give
+ * no stopping rule; this fixed-margin rule is the reading taken here. thr
+ * is formed in float (the scores are float values), and when it is NaN
+ * (s_first = +inf with margin = +inf) nothing is skipped. kept [B,T] (may
+ * be NULL) receives the number of positions kept per query.
  */
-int orc_topk(const double* scores, int B, int T, int kv_len, int k, const int32_t* k_rows,
-             int32_t* idx) {
+int orc_topk_margin(const double* scores, int B, int T, int kv_len, int k, const int32_t* k_rows,
+                    const float* margin, int32_t* idx, int32_t* kept) {
   if (B < 1 || T < 1 || kv_len < T || k < 1) return -1;
+  if (margin && !(*margin >= 0.0f)) return -1;
   orc_cand* c = (orc_cand*)malloc(sizeof(orc_cand) * (size_t)kv_len);
   long* chosen = (long*)malloc(sizeof(long) * (size_t)k);
   if (!c || !chosen) {
@@ -260,15 +277,29 @@ int orc_topk(const double* scores, int B, int T, int kv_len, int k, const int32_
         if (kb > k) kb = k;
       }
       long n = vis < kb ? vis : kb;
+      if (margin && n > 0) {
+        const float thr = (float)c[0].score - *margin;
+        if (thr == thr) { /* not NaN */
+          long r = 0;
+          while (r < n && c[r].score >= (double)thr) r++;
+          n = r;
+        }
+      }
       for (long j = 0; j < n; j++) chosen[j] = c[j].pos;
       qsort(chosen, (size_t)n, sizeof(long), orc_cmp_long);
       int32_t* out = idx + ((size_t)b * T + t) * k;
       for (long j = 0; j < k; j++) out[j] = j < n ? (int32_t)chosen[j] : -1;
+      if (kept) kept[(size_t)b * T + t] = (int32_t)n;
     }
   }
   free(c);
   free(chosen);
   return 0;
+}
+
+int orc_topk(const double* scores, int B, int T, int kv_len, int k, const int32_t* k_rows,
+             int32_t* idx) {
+  return orc_topk_margin(scores, B, T, kv_len, k, k_rows, NULL, idx, NULL);
 }
 
 /* ------------------------------------------------------------------------ */
@@ -361,7 +392,8 @@ int orc_sparse_attn(const void* q, const void* kc, const void* vc, int dtype,
  * nearest F layer at or before l left it.
  * Per-layer arrays hold host pointers to host buffers (F-layer indexer
  * inputs may be NULL for S layers). k_rows (may be NULL) gives each query
- * its own count, as in orc_topk. out[l] [B,T,Hq,D] double, lse[l]
+ * its own count, and skip_margin (may be NULL) the ordered-skipping margin,
+ * as in orc_topk_margin. out[l] [B,T,Hq,D] double, lse[l]
  * [B,T,Hq] double. n_indexer_calls (may be NULL) receives how many times
  * the indexer ran. Returns -1 for an invalid layer map.
  */
@@ -372,8 +404,8 @@ int orc_decode_step(int n_layers, const int32_t* layer_src,
                     const float* const* w, int idx_dtype, int32_t* idx_out,
                     double* const* out, double* const* lse, int B, int T,
                     int Hq, int Hkv, int D, int H_I, int D_I, int kv_len,
-                    int L_cap, int k, const int32_t* k_rows, double scale,
-                    int* n_indexer_calls) {
+                    int L_cap, int k, const int32_t* k_rows, const float* skip_margin,
+                    double scale, int* n_indexer_calls) {
   if (n_layers < 1 || layer_src[0] != 0) return -1;
   int last_f = -1;
   for (int l = 0; l < n_layers; l++) {
@@ -387,7 +419,7 @@ int orc_decode_step(int n_layers, const int32_t* layer_src,
     if (layer_src[l] == l) {
       int rc = orc_index_score(q_idx[l], k_idx[l], idx_dtype, w[l], scores, NULL,
                                B, T, H_I, D_I, kv_len, L_cap);
-      if (rc == 0) rc = orc_topk(scores, B, T, kv_len, k, k_rows, idx_out);
+      if (rc == 0) rc = orc_topk_margin(scores, B, T, kv_len, k, k_rows, skip_margin, idx_out, NULL);
       if (rc) {
         free(scores);
         return rc;

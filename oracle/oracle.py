@@ -47,9 +47,10 @@ def _load():
             lib.orc_decode.argtypes = [P, I, ctypes.c_long, P]
             lib.orc_index_score.argtypes = [P, P, I, P, P, P] + [I] * 6
             lib.orc_topk.argtypes = [P, I, I, I, I, P, P]
+            lib.orc_topk_margin.argtypes = [P, I, I, I, I, P, P, P, P]
             lib.orc_sparse_attn.argtypes = [P, P, P, I, P, I, P, P] + [I] * 7 + [D]
             lib.orc_decode_step.argtypes = (
-                [I, P, P, P, P, I, P, P, P, I, P, P, P] + [I] * 10 + [P, D, P]
+                [I, P, P, P, P, I, P, P, P, I, P, P, P] + [I] * 10 + [P, P, D, P]
             )
             lib.orc_block_union.argtypes = [P, I, I, I, I, I, I, P, P]
             lib.orc_block_attn.argtypes = [P, P, P, I, P, P, I, P, P] + [I] * 7 + [D, I]
@@ -58,6 +59,7 @@ def _load():
                 lib.orc_decode,
                 lib.orc_index_score,
                 lib.orc_topk,
+                lib.orc_topk_margin,
                 lib.orc_sparse_attn,
                 lib.orc_decode_step,
                 lib.orc_block_union,
@@ -128,6 +130,23 @@ def topk(scores, k, kv_len=None, k_rows=None):
     return idx
 
 
+def topk_margin(scores, k, margin, kv_len=None, k_rows=None):
+    """Top-k with ordered skipping (orc_topk_margin). margin: float >= 0, taken
+    as float32. Returns (idx [B,T,k] int32, kept [B,T] int32)."""
+    scores = np.ascontiguousarray(scores, dtype=np.float64)
+    B, T, L = scores.shape
+    kv_len = L if kv_len is None else kv_len
+    if kv_len != L:
+        raise ValueError("topk_margin: scores last dim must equal kv_len")
+    kr = None if k_rows is None else _c(np.asarray(k_rows).reshape(B, T), np.int32)
+    m = np.array([margin], np.float32)
+    idx = np.empty((B, T, k), np.int32)
+    kept = np.empty((B, T), np.int32)
+    _check(_load().orc_topk_margin(_p(scores), B, T, kv_len, k, _p(kr), _p(m), _p(idx), _p(kept)),
+           "topk_margin")
+    return idx, kept
+
+
 def sparse_attn(q, k_cache, v_cache, dtype, idx, kv_len, scale=0.0):
     """Gathered attention. q [B,T,Hq,D], caches [B,L_cap,Hkv,D] raw, idx [B,T,k] int32.
 
@@ -149,7 +168,7 @@ def sparse_attn(q, k_cache, v_cache, dtype, idx, kv_len, scale=0.0):
 
 
 def decode_step(layer_src, q, k_cache, v_cache, dtype, q_idx, k_idx, w, idx_dtype, kv_len, k,
-                scale=0.0, k_rows=None):
+                scale=0.0, k_rows=None, skip_margin=None):
     """One step over len(layer_src) layers sharing routing.
 
     Per-layer lists of numpy arrays (indexer inputs may be None on S layers).
@@ -171,6 +190,7 @@ def decode_step(layer_src, q, k_cache, v_cache, dtype, q_idx, k_idx, w, idx_dtyp
     lses = [np.empty((B, T, Hq), np.float64) for _ in range(n)]
     idx = np.empty((B, T, k), np.int32)
     kr = None if k_rows is None else _c(np.asarray(k_rows).reshape(B, T), np.int32)
+    sm = None if skip_margin is None else np.array([skip_margin], np.float32)
     calls = ctypes.c_int(0)
     VP = ctypes.c_void_p * n
 
@@ -179,7 +199,7 @@ def decode_step(layer_src, q, k_cache, v_cache, dtype, q_idx, k_idx, w, idx_dtyp
 
     rc = _load().orc_decode_step(
         n, _p(src), arr(qs), arr(ks), arr(vs), dtype, arr(qi), arr(ki), arr(ws), idx_dtype, _p(idx),
-        arr(outs), arr(lses), B, T, Hq, Hkv, D, H_I, D_I, kv_len, L_cap, k, _p(kr), float(scale),
+        arr(outs), arr(lses), B, T, Hq, Hkv, D, H_I, D_I, kv_len, L_cap, k, _p(kr), _p(sm), float(scale),
         ctypes.byref(calls),
     )
     _check(rc, "decode_step")
