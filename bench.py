@@ -285,6 +285,30 @@ def main():
                  "ms_per_step_events": e3a.elapsed_time(e3b) / K}
     del step_dk
 
+    # The same step with ordered skipping: the margin is the median over the
+    # first full layer's queries of (best score - score at rank k/2), so the
+    # median query keeps about half of its k positions. Same timing as above.
+    f0 = wl.f_layers[0]
+    sc = clsa.index_score(X.q_idx[f0], X.k_idx[f0], X.w[f0], kv_len=wl.kv_len)
+    top = torch.topk(sc.view(wl.B * wl.T, wl.kv_len), min(wl.k, wl.kv_len - wl.T + 1), dim=1).values
+    margin = float((top[:, 0] - top[:, top.shape[1] // 2 - 1]).median())
+    _, kept = clsa.topk_margin(sc, wl.k, margin)
+    del sc, top
+    step_os = clsa.DecodeStep(wl.layer_src, X.q, X.k_cache, X.v_cache, X.q_idx, X.k_idx, X.w, wl.k,
+                              kv_len=wl.kv_len, skip_margin=margin)
+    for _ in range(W):
+        step_os.run()
+    torch.cuda.synchronize()
+    e4a, e4b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e4a.record()
+    for _ in range(K):
+        step_os.run()
+    e4b.record()
+    torch.cuda.synchronize()
+    ordered_skip = {"margin": margin, "rule": "median query keeps ~k/2 of its top-k",
+                    "mean_kept": float(kept.float().mean()), "ms_per_step_events": e4a.elapsed_time(e4b) / K}
+    del step_os
+
     # Per-kernel averages: R back-to-back calls of one entry point, same
     # shapes and inputs as the step. The R calls are captured once in a HIP
     # graph and replayed between one event pair on the replay stream, so the
@@ -536,6 +560,7 @@ def main():
         "ms_per_step_cold": us_step_cold * 1e-3,
         "dense_gather_context": dense,
         "dynamic_k": dynamic_k,
+        "ordered_skip": ordered_skip,
         "ms_per_step_graph_replay": graph_ms,
     }
     if comparator is not None:

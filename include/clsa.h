@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define CLSA_ABI_VERSION 2
+#define CLSA_ABI_VERSION 3
 
 /* Status codes returned by every entry point. */
 enum clsa_status {
@@ -144,6 +144,28 @@ int clsa_topk_vark(const float* scores, int B, int T, int kv_len, int k,
                    size_t ws_bytes, void* stream);
 
 /*
+ * Ordered skipping (CoSA summary, the paragraphs on the Kernel-Aware Proxy
+ * and the Ordered-Skipping Kernel: the proxy hands the kernel a priority
+ * list, the kernel reads the most important entries first and skips the
+ * rest). The page gives no stopping rule; the one taken here: each query's
+ * selection (as clsa_topk_vark) is read in priority order, score descending
+ * then position ascending, and reading stops at the first entry whose score
+ * is below thr = (the query's best score) - margin, thr computed in float32
+ * (round to nearest). The positions read are written ascending and the rest
+ * of the k-wide row is -1. Since the kept set is decided before attention,
+ * attention visits it in position order; the result equals reading it in
+ * priority order up to float32 summation order.
+ *   margin  >= 0; +INFINITY keeps the whole selection (clsa_topk_vark).
+ *           Negative or NaN: CLSA_ERR_INVALID_ARG.
+ *   kept    device int32 [B, T] output (positions kept per query), or NULL.
+ * If thr is NaN (best score +inf with margin +inf) nothing is skipped.
+ * Same workspace, ordering, scores and other errors as clsa_topk.
+ */
+int clsa_topk_margin(const float* scores, int B, int T, int kv_len, int k,
+                     const int32_t* k_per_query, float margin, int32_t* idx,
+                     int32_t* kept, void* ws, size_t ws_bytes, void* stream);
+
+/*
  * Gathered sparse attention over the selected tokens (IndexCache summary,
  * "1. Problématique": main attention over the k selected tokens, O(Lk);
  * CLSA article, "Comment CLSA fonctionne": every layer after the indexer
@@ -212,6 +234,11 @@ typedef struct clsa_step_desc {
    * device int32 [B, T]; query (b, t) keeps its k_per_query[b, t] best
    * positions (clamped to [0, k]) as in clsa_topk_vark. */
   const int32_t* k_per_query;
+  /* Optional ordered skipping: NULL (off), or a host pointer to the margin
+   * (>= 0) that F layers' top-k apply as in clsa_topk_margin; read during
+   * the call only. With per-query counts or a finite margin, attention skips
+   * the 32-entry steps of an index row that hold no visible position. */
+  const float* skip_margin;
 } clsa_step_desc;
 
 /* Workspace bytes needed by clsa_decode_step for this descriptor (0 if the

@@ -24,8 +24,9 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = clsa.declared_symbols()
-    assert len(names) == 14
-    for required in ("clsa_index_score", "clsa_topk", "clsa_sparse_attn", "clsa_decode_step"):
+    assert len(names) == 15
+    for required in ("clsa_index_score", "clsa_topk", "clsa_topk_margin", "clsa_sparse_attn",
+                     "clsa_decode_step"):
         assert required in names
     raw = ctypes.CDLL(binding.LIB_PATH)
     for n in names:

@@ -20,5 +20,6 @@ from .binding import (  # noqa: F401
     load,
     sparse_attn,
     topk,
+    topk_margin,
     workspace_bytes,
 )

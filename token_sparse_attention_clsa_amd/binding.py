@@ -55,6 +55,7 @@ class StepDesc(ctypes.Structure):
         ("scale", F),
         ("events", ctypes.POINTER(P)),
         ("k_per_query", P),
+        ("skip_margin", ctypes.POINTER(F)),
     ]
 
 
@@ -79,6 +80,7 @@ def load() -> ctypes.CDLL:
         "clsa_index_score": (I, [P, P, I, P, P] + [I] * 6 + [P]),
         "clsa_topk": (I, [P, I, I, I, I, P, P, SZ, P]),
         "clsa_topk_vark": (I, [P, I, I, I, I, P, P, P, SZ, P]),
+        "clsa_topk_margin": (I, [P, I, I, I, I, P, F, P, P, P, SZ, P]),
         "clsa_sparse_attn": (I, [P, P, P, I, P, I, P, P] + [I] * 7 + [F, P, SZ, P]),
         "clsa_decode_step_workspace_bytes": (SZ, [ctypes.POINTER(StepDesc)]),
         "clsa_decode_step": (I, [ctypes.POINTER(StepDesc), P, SZ, P]),
@@ -181,6 +183,31 @@ def topk(scores: torch.Tensor, k: int, out: Optional[torch.Tensor] = None,
     return out
 
 
+def topk_margin(scores: torch.Tensor, k: int, margin: float, out: Optional[torch.Tensor] = None,
+                kept: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None,
+                k_per_query: Optional[torch.Tensor] = None, want_kept: bool = True):
+    """clsa_topk_margin (ordered skipping). scores [B,T,kv_len] f32 ->
+    (idx [B,T,k] int32 ascending, -1 padded; kept [B,T] int32 or None)."""
+    _dev(scores, "scores", (torch.float32,))
+    B, T, L = scores.shape
+    if out is None:
+        out = torch.empty((B, T, k), dtype=torch.int32, device=scores.device)
+    _dev(out, "idx", (torch.int32,), (B, T, k))
+    if kept is None and want_kept:
+        kept = torch.empty((B, T), dtype=torch.int32, device=scores.device)
+    if kept is not None:
+        _dev(kept, "kept", (torch.int32,), (B, T))
+    if k_per_query is not None:
+        _dev(k_per_query, "k_per_query", (torch.int32,), (B, T))
+    need = workspace_bytes(OP_TOPK, B=B, T=T, kv_len=L, k=k)
+    if ws is None:
+        ws = _workspace(need, scores.device)
+    rc = load().clsa_topk_margin(_ptr(scores), B, T, L, k, _ptr(k_per_query), float(margin), _ptr(out),
+                                 _ptr(kept), _ptr(ws), ws.numel(), _stream())
+    _check(rc, "clsa_topk_margin")
+    return out, kept
+
+
 def sparse_attn(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, idx: torch.Tensor,
                 kv_len: Optional[int] = None, scale: float = 0.0, out: Optional[torch.Tensor] = None,
                 lse: Optional[torch.Tensor] = None, want_lse: bool = True,
@@ -220,12 +247,15 @@ class DecodeStep:
     tensors on F layers and None on S layers. ``run()`` enqueues one step on
     torch's current stream; outputs live in ``self.out`` / ``self.lse`` and the
     index cache in ``self.idx``. ``k_per_query`` (int32 [B, T], optional) gives
-    each query its own count of kept positions (as clsa_topk_vark).
+    each query its own count of kept positions (as clsa_topk_vark);
+    ``skip_margin`` (float >= 0, optional) turns on ordered skipping (as
+    clsa_topk_margin) in the F layers' top-k.
     """
 
     def __init__(self, layer_src: Sequence[int], q, k_cache, v_cache, q_idx, k_idx, w, k: int,
                  kv_len: Optional[int] = None, scale: float = 0.0, want_lse: bool = True,
-                 events: Optional[Sequence] = None, k_per_query: Optional[torch.Tensor] = None):
+                 events: Optional[Sequence] = None, k_per_query: Optional[torch.Tensor] = None,
+                 skip_margin: Optional[float] = None):
         n = len(layer_src)
         self.n = n
         dev = q[0].device
@@ -261,6 +291,7 @@ class DecodeStep:
         self._qi = PA(*[0 if t is None else t.data_ptr() for t in q_idx])
         self._ki = PA(*[0 if t is None else t.data_ptr() for t in k_idx])
         self._w = PA(*[0 if t is None else t.data_ptr() for t in w])
+        self._margin = None if skip_margin is None else ctypes.pointer(F(float(skip_margin)))
         self._ev = None
         if events is not None:
             if len(events) != 4 * n:
@@ -275,7 +306,8 @@ class DecodeStep:
             self._qi, self._ki, self._w, self.idx.data_ptr(),
             _DT[q[0].dtype], _DT[q_idx[f0].dtype], B, T, Hq, Hkv, D, H_I, D_I, kv_len, L_cap, k,
             float(scale), self._ev if self._ev is not None else ctypes.POINTER(P)(),
-            None if k_per_query is None else k_per_query.data_ptr())
+            None if k_per_query is None else k_per_query.data_ptr(),
+            ctypes.POINTER(F)() if skip_margin is None else self._margin)
         lib = load()
         need = lib.clsa_decode_step_workspace_bytes(ctypes.byref(self.desc))
         if need == 0:

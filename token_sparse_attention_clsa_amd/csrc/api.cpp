@@ -198,26 +198,36 @@ int clsa_index_score(const void* q_idx, const void* k_idx, int idx_dtype, const 
                             static_cast<hipStream_t>(stream));
 }
 
-int clsa_topk_vark(const float* scores, int B, int T, int kv_len, int k, const int32_t* k_per_query,
-                   int32_t* idx, void* ws, size_t ws_bytes, void* stream) {
+int clsa_topk_margin(const float* scores, int B, int T, int kv_len, int k,
+                     const int32_t* k_per_query, float margin, int32_t* idx, int32_t* kept, void* ws,
+                     size_t ws_bytes, void* stream) {
   int rc = check_topk_args(scores, B, T, kv_len, k, idx);
   if (rc) return rc;
   if (k_per_query && !aligned(k_per_query, 4))
     return set_error(CLSA_ERR_INVALID_ARG, "topk: misaligned k_per_query");
+  if (kept && !aligned(kept, 4)) return set_error(CLSA_ERR_INVALID_ARG, "topk: misaligned kept");
+  if (!(margin >= 0.f)) return set_error(CLSA_ERR_INVALID_ARG, "topk: margin must be >= 0 (or +inf)");
   const TopkWs L = topk_ws(B * T, kv_len);
   if (!ws || ws_bytes < L.total || !aligned(ws, 256))
     return set_error(CLSA_ERR_WORKSPACE, "topk: workspace of %zu bytes (256-aligned) required, got %zu",
                      L.total, ws ? ws_bytes : (size_t)0);
   char* base = static_cast<char*>(ws);
-  return launch_topk(scores, B, T, kv_len, k, k_per_query, idx,
+  return launch_topk(scores, B, T, kv_len, k, k_per_query, margin, idx, kept,
                      reinterpret_cast<uint32_t*>(base + L.counts),
                      reinterpret_cast<int32_t*>(base + L.cand),
                      reinterpret_cast<int32_t*>(base + L.spill), static_cast<hipStream_t>(stream));
 }
 
+int clsa_topk_vark(const float* scores, int B, int T, int kv_len, int k, const int32_t* k_per_query,
+                   int32_t* idx, void* ws, size_t ws_bytes, void* stream) {
+  return clsa_topk_margin(scores, B, T, kv_len, k, k_per_query, INFINITY, idx, nullptr, ws, ws_bytes,
+                          stream);
+}
+
 int clsa_topk(const float* scores, int B, int T, int kv_len, int k, int32_t* idx, void* ws,
               size_t ws_bytes, void* stream) {
-  return clsa_topk_vark(scores, B, T, kv_len, k, nullptr, idx, ws, ws_bytes, stream);
+  return clsa_topk_margin(scores, B, T, kv_len, k, nullptr, INFINITY, idx, nullptr, ws, ws_bytes,
+                          stream);
 }
 
 int clsa_sparse_attn(const void* q, const void* k_cache, const void* v_cache, int dtype,
@@ -280,6 +290,8 @@ static int check_step(const clsa_step_desc* d) {
     return set_error(CLSA_ERR_INVALID_ARG, "decode_step: scale must be finite");
   if (d->k_per_query && !aligned(d->k_per_query, 4))
     return set_error(CLSA_ERR_INVALID_ARG, "decode_step: misaligned k_per_query");
+  if (d->skip_margin && !(*d->skip_margin >= 0.f))
+    return set_error(CLSA_ERR_INVALID_ARG, "decode_step: skip_margin must be >= 0 (or +inf)");
   return CLSA_OK;
 }
 
@@ -303,6 +315,10 @@ int clsa_decode_step(const clsa_step_desc* d, void* ws, size_t ws_bytes, void* s
   int32_t* spill = reinterpret_cast<int32_t*>(base + L.topk.spill);
   float* partials = reinterpret_cast<float*>(base + L.partials);
   float* scores = reinterpret_cast<float*>(base + L.scores);
+  const float margin = d->skip_margin ? *d->skip_margin : INFINITY;
+  // Per-query counts or a finite margin leave -1 tails in the index rows:
+  // attention then skips 32-entry steps holding no visible entry.
+  const bool skip_empty = d->k_per_query != nullptr || margin < INFINITY;
   for (int l = 0; l < d->n_layers; l++) {
     if ((rc = record(d->events, 4 * l, s))) return rc;
     if (d->layer_src[l] == l) {
@@ -310,8 +326,8 @@ int clsa_decode_step(const clsa_step_desc* d, void* ws, size_t ws_bytes, void* s
                               d->H_I, d->D_I, d->kv_len, d->L_cap, s);
       if (rc) return rc;
       if ((rc = record(d->events, 4 * l + 1, s))) return rc;
-      rc = launch_topk(scores, d->B, d->T, d->kv_len, d->k, d->k_per_query, d->idx_out, counts, cand,
-                       spill, s);
+      rc = launch_topk(scores, d->B, d->T, d->kv_len, d->k, d->k_per_query, margin, d->idx_out,
+                       nullptr, counts, cand, spill, s);
       if (rc) return rc;
     } else if ((rc = record(d->events, 4 * l + 1, s))) {
       return rc;
@@ -319,8 +335,7 @@ int clsa_decode_step(const clsa_step_desc* d, void* ws, size_t ws_bytes, void* s
     if ((rc = record(d->events, 4 * l + 2, s))) return rc;
     rc = launch_sparse_attn(d->q[l], d->k_cache[l], d->v_cache[l], d->dtype, d->idx_out, d->k,
                             d->out[l], d->lse ? d->lse[l] : nullptr, d->B, d->T, d->Hq, d->Hkv,
-                            d->D, d->kv_len, d->L_cap, d->scale, partials,
-                            d->k_per_query != nullptr, s);
+                            d->D, d->kv_len, d->L_cap, d->scale, partials, skip_empty, s);
     if (rc) return rc;
     if ((rc = record(d->events, 4 * l + 3, s))) return rc;
   }

@@ -38,8 +38,12 @@ struct TopkBuffers {
 };
 TopkBuffers topk_buffers(int rows, int kv_len);
 // k_rows: NULL, or a device int32 [B*T] of per-row counts (clamped to [0, k]).
+// margin: +inf, or the ordered-skipping margin (>= 0): each row keeps only the
+// selected positions scoring at least (row maximum - margin). kept: NULL, or
+// a device int32 [B*T] receiving each row's count of kept positions.
 int launch_topk(const float* scores, int B, int T, int kv_len, int k, const int32_t* k_rows,
-                int32_t* idx, uint32_t* counts, int32_t* cand, int32_t* spill, hipStream_t stream);
+                float margin, int32_t* idx, int32_t* kept, uint32_t* counts, int32_t* cand,
+                int32_t* spill, hipStream_t stream);
 
 // ---- sparse attention --------------------------------------------------------
 // Buffer: partials [attn_partial_floats(...)] f32 (split states; unused when

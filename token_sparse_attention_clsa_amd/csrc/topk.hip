@@ -31,6 +31,15 @@
 // Rows whose visible count is <= k take every visible position. With a
 // per-row count k_rows[row] (clamped to [0, k]), a row keeps its k_rows[row]
 // best positions and the rest of its k slots hold -1.
+// Ordered skipping (CoSA summary, the paragraphs on its proxy and its
+// kernel): with a finite margin, the selection read in priority order (score
+// descending, position ascending) stops at the first entry whose score is
+// below thr = (row maximum) - margin, thr formed in float32. The kept
+// entries are exactly the selected keys >= key(thr): when key(thr) is above
+// theta, theta becomes key(thr) and every key equal to it is taken; the rest
+// of the row is -1.
+#include <climits>
+
 #include "kernels.h"
 
 namespace clsa {
@@ -111,6 +120,18 @@ __global__ __launch_bounds__(256) void fill_zero(uint32_t* p, size_t n) {
     p[i] = 0u;
 }
 
+// The score whose key is `key` (inverse of score_key; -0 comes back as +0).
+__device__ __forceinline__ float key_score(uint32_t key) {
+  return __uint_as_float((key & 0x80000000u) ? (key & 0x7fffffffu) : ~key);
+}
+// Key of the ordered-skipping threshold (row maximum key mx) - margin, or 0
+// (every key passes) when the margin is +inf or the threshold is NaN.
+__device__ __forceinline__ uint32_t margin_key(uint32_t mx, float margin) {
+  if (!(margin < INFINITY)) return 0u;
+  const float thr = key_score(mx) - margin;
+  return thr == thr ? score_key(thr) : 0u;
+}
+
 // Candidates: the first kLdsCap in LDS, the rest in the workspace (their
 // keys are read back from the scores).
 struct Cand {
@@ -142,10 +163,13 @@ struct SegCand {
 
 // Resolves theta, the need-th largest key among the candidates, all of
 // which in play lie in [lo, lo + R) (R a power of two <= 2^32), by radix
-// passes of at most 12 bits on key - lo, then emits the row's selection.
+// passes of at most 12 bits on key - lo, then emits the row's selection:
+// its k best keys, or with mkey above theta (ordered skipping) only the keys
+// >= mkey, the rest of the k slots -1. kept (or NULL) receives the count.
 template <class Acc>
 __device__ void select_and_emit(const Acc& acc, int n, int need, uint32_t lo, uint64_t R,
-                                uint32_t* h, int* res, int* tmp, int32_t* out, int k) {
+                                uint32_t* h, int* res, int* tmp, int32_t* out, int k,
+                                uint32_t mkey, int32_t* kept) {
   __shared__ uint32_t few[kWave];
   __shared__ int nfew;
   while (R > 1) {  // uniform over the workgroup
@@ -196,8 +220,12 @@ __device__ void select_and_emit(const Acc& acc, int n, int need, uint32_t lo, ui
       R = 1;
     }
   }
-  const uint32_t theta = lo;
-  const int quota = need;  // how many keys equal to theta are taken
+  uint32_t theta = lo;
+  int quota = need;  // how many keys equal to theta are taken
+  if (mkey > theta) {  // uniform: reading stops before theta
+    theta = mkey;
+    quota = INT_MAX;
+  }
   // Ordered emission: thread t owns the run [t0 + t * run, t0 + (t + 1) * run)
   // of the tile (run <= 16), so up to 16 * kThreads candidates take one
   // block scan and no barrier waits behind the output stores.
@@ -233,6 +261,9 @@ __device__ void select_and_emit(const Acc& acc, int n, int need, uint32_t lo, ui
     gt_base += tot & 0xffff;
     eq_base += tot >> 16;
   }
+  const int nk = min(k, gt_base + min(eq_base, quota));  // k unless mkey cut the row
+  for (int i = nk + threadIdx.x; i < k; i += kThreads) out[i] = -1;
+  if (kept && threadIdx.x == 0) *kept = nk;
 }
 
 // Selection of the k largest among n >= k candidates whose keys lie in
@@ -242,10 +273,10 @@ __device__ void select_and_emit(const Acc& acc, int n, int need, uint32_t lo, ui
 // or one when the bin it leaves holds at most 64 keys.
 template <class Acc>
 __device__ void select_top(const Acc& acc, int n, int k, uint32_t mn, uint32_t mx, uint32_t* h,
-                           int* res, int* tmp, int32_t* out) {
+                           int* res, int* tmp, int32_t* out, uint32_t mkey, int32_t* kept) {
   const uint64_t span = (uint64_t)(mx - mn) + 1;  // n >= k >= 1, so mx >= mn
   const uint64_t R = span == 1 ? 1 : 1ull << (64 - __clzll(span - 1));
-  select_and_emit(acc, n, k, mn, R, h, res, tmp, out, k);
+  select_and_emit(acc, n, k, mn, R, h, res, tmp, out, k, mkey, kept);
 }
 
 // Block-wide min and max of the threads' (mn, mx); ends with a barrier
@@ -510,7 +541,8 @@ __global__ __launch_bounds__(kThreads) void topk_select(const float* __restrict_
                                                         int32_t* __restrict__ idx, int T,
                                                         int kv_len, int k,
                                                         const int32_t* __restrict__ k_rows,
-                                                        int nchunks) {
+                                                        int nchunks, float margin,
+                                                        int32_t* __restrict__ kept) {
   __shared__ __attribute__((aligned(16))) uint32_t h[kBins0 * (1 + kHistCopies)];
   __shared__ int32_t lpos[kLdsCap];
   __shared__ uint32_t lkey[kLdsCap];
@@ -522,17 +554,43 @@ __global__ __launch_bounds__(kThreads) void topk_select(const float* __restrict_
   const int row = blockIdx.x;
   const int vis = kv_len - T + (row % T) + 1;
   int32_t* out = idx + (size_t)row * k;  // k slots
+  int32_t* kept_row = kept ? kept + row : nullptr;
   if (k_rows) {  // this row keeps kr positions; slots kr .. k-1 hold -1
     const int kr = min(max(k_rows[row], 0), k);
     for (int i = kr + threadIdx.x; i < k; i += kThreads) out[i] = -1;
     k = kr;
-    if (k == 0) return;
-  }
-  if (vis <= k) {  // every visible position, in order
-    for (int i = threadIdx.x; i < k; i += kThreads) out[i] = i < vis ? i : -1;
-    return;
+    if (k == 0) {
+      if (kept_row && threadIdx.x == 0) *kept_row = 0;
+      return;
+    }
   }
   const float* srow = scores + (size_t)row * kv_len;
+  const bool skip = margin < INFINITY;  // ordered skipping (uniform)
+  if (vis <= k) {  // every visible position, in order
+    if (!skip) {
+      for (int i = threadIdx.x; i < k; i += kThreads) out[i] = i < vis ? i : -1;
+      if (kept_row && threadIdx.x == 0) *kept_row = vis;
+      return;
+    }
+    // ... those at or above the threshold: row maximum, then an ordered
+    // compaction of the visible positions.
+    uint32_t mn = 0xffffffffu, mx = 0u;
+    for (int i = threadIdx.x; i < vis; i += kThreads) mx = max(mx, score_key(srow[i]));
+    block_minmax(mn, mx, mm);
+    const uint32_t mkey = margin_key(mx, margin);
+    int base = 0;
+    for (int t0 = 0; t0 < vis; t0 += kThreads) {  // uniform
+      const int i = t0 + threadIdx.x;
+      const int f = i < vis && score_key(srow[i]) >= mkey;
+      int tot;
+      const int pre = block_exclusive_scan<kThreads>(f, tmp, &tot);
+      if (f) out[base + pre] = i;
+      base += tot;
+    }
+    for (int i = base + threadIdx.x; i < k; i += kThreads) out[i] = -1;
+    if (kept_row && threadIdx.x == 0) *kept_row = base;
+    return;
+  }
   // Chunk owned by this thread for the gather: tpc threads per chunk, thread
   // j0 of a chunk takes entries j0, j0 + tpc, ... Its first kSpec entries are
   // loaded now, before the counts are known (the slots exist whatever the
@@ -583,7 +641,8 @@ __global__ __launch_bounds__(kThreads) void topk_select(const float* __restrict_
         }
       }
       block_minmax(mn, mx, mm);  // its barrier also publishes the gather
-      select_top(Cand{lpos, lkey, nullptr, srow}, n, k, mn, mx, h, res, tmp, out);
+      select_top(Cand{lpos, lkey, nullptr, srow}, n, k, mn, mx, h, res, tmp, out,
+                 margin_key(mx, margin), kept_row);
     } else {
       const SegCand acc{segs, off, nchunks};
       for (int i = threadIdx.x; i < n; i += kThreads) {
@@ -592,7 +651,7 @@ __global__ __launch_bounds__(kThreads) void topk_select(const float* __restrict_
         mx = max(mx, key);
       }
       block_minmax(mn, mx, mm);
-      select_top(acc, n, k, mn, mx, h, res, tmp, out);
+      select_top(acc, n, k, mn, mx, h, res, tmp, out, margin_key(mx, margin), kept_row);
     }
     return;
   }
@@ -605,8 +664,15 @@ __global__ __launch_bounds__(kThreads) void topk_select(const float* __restrict_
     n = histogram_and_candidates<true>(srow, vis, k, h, lpos, lkey, gpos, wtot, tmp, res, &b0, &above);
   else
     n = histogram_and_candidates<false>(srow, vis, k, h, lpos, lkey, gpos, wtot, tmp, res, &b0, &above);
-  select_and_emit(Cand{lpos, lkey, gpos, srow}, n, k - above, b0 << 20, 1ull << 20, h, res, tmp,
-                  out, k);
+  const Cand acc{lpos, lkey, gpos, srow};
+  uint32_t mkey = 0u;
+  if (skip) {  // the row maximum is among the candidates (the top bins)
+    uint32_t mn = 0xffffffffu, mx = 0u;
+    for (int i = threadIdx.x; i < n; i += kThreads) mx = max(mx, acc.k(i));
+    block_minmax(mn, mx, mm);
+    mkey = margin_key(mx, margin);
+  }
+  select_and_emit(acc, n, k - above, b0 << 20, 1ull << 20, h, res, tmp, out, k, mkey, kept_row);
 }
 
 }  // namespace
@@ -629,7 +695,8 @@ TopkBuffers topk_buffers(int rows, int kv_len) {
 }
 
 int launch_topk(const float* scores, int B, int T, int kv_len, int k, const int32_t* k_rows,
-                int32_t* idx, uint32_t* counts, int32_t* cand, int32_t* spill, hipStream_t stream) {
+                float margin, int32_t* idx, int32_t* kept, uint32_t* counts, int32_t* cand,
+                int32_t* spill, hipStream_t stream) {
   const int rows = B * T;
   const TopkBuffers tb = topk_buffers(rows, kv_len);
   if (tb.nchunks > kTopkMaxChunks)
@@ -645,7 +712,7 @@ int launch_topk(const float* scores, int B, int T, int kv_len, int k, const int3
   int rc = check_launch("topk_filter");
   if (rc) return rc;
   hipLaunchKernelGGL(topk_select, dim3(rows), dim3(kThreads), 0, stream, scores, counts, segs, spill,
-                     idx, T, kv_len, k, k_rows, tb.nchunks);
+                     idx, T, kv_len, k, k_rows, tb.nchunks, margin, kept);
   return check_launch("topk_select");
 }
 
