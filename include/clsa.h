@@ -236,8 +236,9 @@ typedef struct clsa_step_desc {
   const int32_t* k_per_query;
   /* Optional ordered skipping: NULL (off), or a host pointer to the margin
    * (>= 0) that F layers' top-k apply as in clsa_topk_margin; read during
-   * the call only. With per-query counts or a finite margin, attention skips
-   * the 32-entry steps of an index row that hold no visible position. */
+   * the call only. With per-query counts or a finite margin, the top-k keeps
+   * each query's count in the workspace and attention reads only that many
+   * entries of its index row. */
   const float* skip_margin;
 } clsa_step_desc;
 

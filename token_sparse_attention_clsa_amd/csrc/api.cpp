@@ -68,7 +68,7 @@ AttnWs attn_ws(int B, int T, int Hq, int Hkv, int k) {
 // scores.
 struct StepWs {
   TopkWs topk;
-  size_t partials, scores, total;
+  size_t partials, scores, kept, total;
 };
 StepWs step_ws(int B, int T, int Hq, int Hkv, int kv_len, int k) {
   StepWs w;
@@ -77,6 +77,7 @@ StepWs step_ws(int B, int T, int Hq, int Hkv, int kv_len, int k) {
   c.off = w.topk.total;
   w.partials = c.add(attn_partial_floats(B, T, Hq, Hkv, k) * 4);
   w.scores = c.add((size_t)B * T * kv_len * 4);
+  w.kept = c.add((size_t)B * T * 4);
   w.total = c.off;
   return w;
 }
@@ -246,7 +247,7 @@ int clsa_sparse_attn(const void* q, const void* k_cache, const void* v_cache, in
                      ws ? ws_bytes : (size_t)0);
   char* base = static_cast<char*>(ws);
   return launch_sparse_attn(q, k_cache, v_cache, dtype, idx, k, out, lse, B, T, Hq, Hkv, D, kv_len,
-                            L_cap, scale, reinterpret_cast<float*>(base + L.partials), false,
+                            L_cap, scale, reinterpret_cast<float*>(base + L.partials), nullptr,
                             static_cast<hipStream_t>(stream));
 }
 
@@ -317,8 +318,11 @@ int clsa_decode_step(const clsa_step_desc* d, void* ws, size_t ws_bytes, void* s
   float* scores = reinterpret_cast<float*>(base + L.scores);
   const float margin = d->skip_margin ? *d->skip_margin : INFINITY;
   // Per-query counts or a finite margin leave -1 tails in the index rows:
-  // attention then skips 32-entry steps holding no visible entry.
-  const bool skip_empty = d->k_per_query != nullptr || margin < INFINITY;
+  // the top-k then writes each row's count and attention reads only that
+  // many entries (the counts stay with the index for the S layers).
+  int32_t* kept = d->k_per_query != nullptr || margin < INFINITY
+                      ? reinterpret_cast<int32_t*>(base + L.kept)
+                      : nullptr;
   for (int l = 0; l < d->n_layers; l++) {
     if ((rc = record(d->events, 4 * l, s))) return rc;
     if (d->layer_src[l] == l) {
@@ -327,7 +331,7 @@ int clsa_decode_step(const clsa_step_desc* d, void* ws, size_t ws_bytes, void* s
       if (rc) return rc;
       if ((rc = record(d->events, 4 * l + 1, s))) return rc;
       rc = launch_topk(scores, d->B, d->T, d->kv_len, d->k, d->k_per_query, margin, d->idx_out,
-                       nullptr, counts, cand, spill, s);
+                       kept, counts, cand, spill, s);
       if (rc) return rc;
     } else if ((rc = record(d->events, 4 * l + 1, s))) {
       return rc;
@@ -335,7 +339,7 @@ int clsa_decode_step(const clsa_step_desc* d, void* ws, size_t ws_bytes, void* s
     if ((rc = record(d->events, 4 * l + 2, s))) return rc;
     rc = launch_sparse_attn(d->q[l], d->k_cache[l], d->v_cache[l], d->dtype, d->idx_out, d->k,
                             d->out[l], d->lse ? d->lse[l] : nullptr, d->B, d->T, d->Hq, d->Hkv,
-                            d->D, d->kv_len, d->L_cap, d->scale, partials, skip_empty, s);
+                            d->D, d->kv_len, d->L_cap, d->scale, partials, kept, s);
     if (rc) return rc;
     if ((rc = record(d->events, 4 * l + 3, s))) return rc;
   }

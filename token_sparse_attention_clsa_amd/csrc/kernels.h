@@ -50,18 +50,19 @@ int launch_topk(const float* scores, int B, int T, int kv_len, int k, const int3
 // the k entries are not split).
 struct AttnSplit {
   int splits, rows_per_split;
-  int waves_per_head;     // waves sharing one split of one KV head
-  bool skip_empty_steps;  // bf16: skip 32-entry steps with no visible entry
+  int waves_per_head;  // waves sharing one split of one KV head
 };
 AttnSplit attn_split(int B, int T, int Hkv, int k, bool mfma);
 size_t attn_partial_floats(int B, int T, int Hq, int Hkv, int k);
 bool sparse_attn_supported(int dtype, int Hq, int Hkv, int D);
-// skip_empty_steps: the index rows may end in long -1 tails (per-query
-// counts below k); bf16 then skips 32-entry steps with no visible entry.
+// row_len: NULL, or a device int32 [B*T] of per-row entry counts for index
+// rows whose entries past their count are all -1 (as the top-k writes them
+// with per-query counts or a margin); only the first row_len[row] entries
+// (clamped to [0, k]) are read.
 int launch_sparse_attn(const void* q, const void* kc, const void* vc, int dtype, const int32_t* idx,
                        int k, void* out, float* lse, int B, int T, int Hq, int Hkv, int D,
-                       int kv_len, int L_cap, float scale, float* partials, bool skip_empty_steps,
-                       hipStream_t stream);
+                       int kv_len, int L_cap, float scale, float* partials,
+                       const int32_t* row_len, hipStream_t stream);
 
 // ---- block union comparator ----------------------------------------------------
 size_t block_union_ws_bytes(int B, int kv_len, int block);

@@ -158,6 +158,13 @@ struct HeadState {
   }
 };
 
+// Entries of index row bt that can hold a position: k, or with per-row counts
+// (rows whose entries past their count are all -1) row_len[bt] clamped to
+// [0, k], so the -1 tail is neither read nor gathered.
+__device__ __forceinline__ int row_count(const int32_t* row_len, int bt, int k) {
+  return row_len ? min(max(row_len[bt], 0), k) : k;
+}
+
 // Split kernel of the index path.
 // grid (S, B*T, Hkv / NW), block 64 * NW; wave w handles KV head
 // g = blockIdx.z * NW + w over entries [split*rows, split*rows + rows) of the
@@ -166,9 +173,9 @@ struct HeadState {
 template <int DT, int G>
 __global__ __launch_bounds__(kWave * kMaxWaves) void attn_split_kernel(
     const char* __restrict__ q, const char* __restrict__ kc, const char* __restrict__ vc,
-    const int32_t* __restrict__ idx, int k, void* __restrict__ out, float* __restrict__ lse,
-    int T, int Hkv, int kv_len, int L_cap, float c_log2, int rows_per_split,
-    float* __restrict__ partials, int nw) {
+    const int32_t* __restrict__ idx, const int32_t* __restrict__ row_len, int k,
+    void* __restrict__ out, float* __restrict__ lse, int T, int Hkv, int kv_len, int L_cap,
+    float c_log2, int rows_per_split, float* __restrict__ partials, int nw) {
   // nw: waves (KV heads) per workgroup, passed rather than read from blockDim.x.
   using E = AttnElem<DT>;
   constexpr int RPI = G <= 4 ? E::rows_per_step : 4;  // fewer rows in flight for 8 heads
@@ -185,7 +192,7 @@ __global__ __launch_bounds__(kWave * kMaxWaves) void attn_split_kernel(
   const int vis = kv_len - T + t + 1;
   const int Hq = Hkv * G;
   const int r0 = split * rows_per_split;
-  const int r1 = min(k, r0 + rows_per_split);
+  const int r1 = min(row_count(row_len, bt, k), r0 + rows_per_split);
   const int32_t* irow = idx + (size_t)bt * k;
 
   typename E::Frag qf[G];
@@ -325,19 +332,20 @@ struct KvStep {
 // This lane's raw index entries of one 32-entry step (entries e0 .. e0 + 31
 // of the query's row): the K row entry of each 16-key tile and the 4 V row
 // entries of its lane group in each tile. Every load is unconditional
-// (entries past `end` read entry end - 1; end >= 1) and the values are
-// masked only when the step is issued.
+// (entries past `end` read entry max(end - 1, 0)) and the values are masked
+// only when the step is issued.
 struct IdxStep {
   int k[2];
   int v[2][4];
 };
 __device__ __forceinline__ void idx_fetch(IdxStep& x, const int32_t* irow, int e0, int end, int col,
                                           int grp) {
+  const int last = max(end - 1, 0);
 #pragma unroll
   for (int tt = 0; tt < 2; tt++) {
-    x.k[tt] = irow[min(e0 + 16 * tt + col, end - 1)];
+    x.k[tt] = irow[min(e0 + 16 * tt + col, last)];
 #pragma unroll
-    for (int r = 0; r < 4; r++) x.v[tt][r] = irow[min(e0 + 16 * tt + 4 * grp + r, end - 1)];
+    for (int r = 0; r < 4; r++) x.v[tt][r] = irow[min(e0 + 16 * tt + 4 * grp + r, last)];
   }
 }
 // Entry e with raw position p: the position if e is before `end` and p is
@@ -347,13 +355,8 @@ __device__ __forceinline__ int vis_pos(int p, int e, int end, int vis) {
 }
 
 // Issues the K/V loads of the step at entries [e0, e0 + 32) from its index
-// entries x. With SKIP, returns false and issues no load when none of the 32
-// entries is visible (e.g. the -1 tail of a query that keeps fewer than k
-// positions); the result is uniform over the wave. Without SKIP the step is
-// always loaded (masked entries read row 0), which keeps the fixed-k code
-// free of the branch.
-template <bool SKIP>
-__device__ __forceinline__ bool kv_issue(KvStep& f, const IdxStep& x, int e0, int end, int vis,
+// entries x (masked entries read cache row 0).
+__device__ __forceinline__ void kv_issue(KvStep& f, const IdxStep& x, int e0, int end, int vis,
                                          int col, int grp, const char* kb, const char* vb,
                                          size_t tok) {
   int kp[2], vp[2][4];
@@ -368,9 +371,6 @@ __device__ __forceinline__ bool kv_issue(KvStep& f, const IdxStep& x, int e0, in
   for (int tt = 0; tt < 2; tt++)
 #pragma unroll
     for (int r = 0; r < 4; r++) f.valid |= (vp[tt][r] >= 0 ? 1u : 0u) << (4 * tt + r);
-  if constexpr (SKIP) {
-    if (__ballot(f.valid != 0u) == 0) return false;
-  }
 #pragma unroll
   for (int tt = 0; tt < 2; tt++)
 #pragma unroll
@@ -382,7 +382,6 @@ __device__ __forceinline__ bool kv_issue(KvStep& f, const IdxStep& x, int e0, in
 #pragma unroll
     for (int r = 0; r < 4; r++)
       f.vf[tt][r] = *reinterpret_cast<const uint4*>(vb + (size_t)max(vp[tt][r], 0) * tok);
-  return true;
 }
 
 // Running state of one wave: O^T accumulators, max and sum of head col.
@@ -468,12 +467,12 @@ __device__ __forceinline__ void kv_consume(const KvStep& f, MfmaState& st, const
 // steps w, w + W, ... and the W states are merged through LDS before the
 // split's single state is written (W > 1 keeps many waves in flight with
 // few splits, so fewer states go through memory).
-template <int G, int W, bool SKIP>
+template <int G, int W>
 __global__ __launch_bounds__(kWave * kMaxWaves) void attn_split_mfma(
     const char* __restrict__ q, const char* __restrict__ kc, const char* __restrict__ vc,
-    const int32_t* __restrict__ idx, int k, void* __restrict__ out, float* __restrict__ lse,
-    int T, int Hkv, int kv_len, int L_cap, float c_log2, int rows_per_split,
-    float* __restrict__ partials, int gpw) {
+    const int32_t* __restrict__ idx, const int32_t* __restrict__ row_len, int k,
+    void* __restrict__ out, float* __restrict__ lse, int T, int Hkv, int kv_len, int L_cap,
+    float c_log2, int rows_per_split, float* __restrict__ partials, int gpw) {
   // gpw: KV heads per workgroup (blockDim.x = 64 * W * gpw). It is an argument
   // rather than derived from blockDim.x, whose read from the dispatch's hidden
   // arguments is a vector load the whole prologue would wait for.
@@ -492,7 +491,7 @@ __global__ __launch_bounds__(kWave * kMaxWaves) void attn_split_mfma(
   const int vis = kv_len - T + t + 1;
   const int Hq = Hkv * G;
   const int r0 = split * rows_per_split;
-  const int r1 = min(k, r0 + rows_per_split);
+  const int r1 = min(row_count(row_len, bt, k), r0 + rows_per_split);
   const int32_t* irow = idx + (size_t)bt * k;
   char* vt = s_vt + wave * kVtBytes;
 
@@ -531,8 +530,8 @@ __global__ __launch_bounds__(kWave * kMaxWaves) void attn_split_mfma(
   // where a wave runs 128 steps).
   for (int e0 = r0 + 32 * w; e0 < r1; e0 += 32 * W) {  // uniform over the wave
     KvStep f;
-    if (kv_issue<SKIP>(f, xi, e0, r1, vis, col, grp, kb, vb, tok))
-      kv_consume(f, st, qf, vt, wbase, rbase, c_log2);
+    kv_issue(f, xi, e0, r1, vis, col, grp, kb, vb, tok);
+    kv_consume(f, st, qf, vt, wbase, rbase, c_log2);
     idx_fetch(xi, irow, e0 + 32 * W, r1, col, grp);
   }
   float l = xgroup_sum(st.l);
@@ -667,7 +666,8 @@ int heads_per_block(int Hkv, int W) {
 }
 
 template <int DT, int G>
-int launch_index_path(const void* q, const void* kc, const void* vc, const int32_t* idx, int k,
+int launch_index_path(const void* q, const void* kc, const void* vc, const int32_t* idx,
+                      const int32_t* row_len, int k,
                       void* out, float* lse, int B, int T, int Hkv, int kv_len, int L_cap,
                       float c_log2, const AttnSplit& sp, float* partials, hipStream_t stream) {
   const int gpw = heads_per_block(Hkv, sp.waves_per_head);
@@ -675,16 +675,10 @@ int launch_index_path(const void* q, const void* kc, const void* vc, const int32
   const dim3 block(kWave * gpw * sp.waves_per_head);
   if constexpr (DT == CLSA_BF16) {
 #define CLSA_SPLIT_MFMA(W)                                                                   \
-  if (sp.skip_empty_steps)                                                                   \
-    hipLaunchKernelGGL((attn_split_mfma<G, W, true>), grid, block, 0, stream,                \
-                       static_cast<const char*>(q), static_cast<const char*>(kc),            \
-                       static_cast<const char*>(vc), idx, k, out, lse, T, Hkv, kv_len, L_cap, \
-                       c_log2, sp.rows_per_split, partials, gpw);                            \
-  else                                                                                       \
-  hipLaunchKernelGGL((attn_split_mfma<G, W, false>), grid, block, 0, stream,                 \
+  hipLaunchKernelGGL((attn_split_mfma<G, W>), grid, block, 0, stream,                        \
                      static_cast<const char*>(q), static_cast<const char*>(kc),              \
-                     static_cast<const char*>(vc), idx, k, out, lse, T, Hkv, kv_len, L_cap,  \
-                     c_log2, sp.rows_per_split, partials, gpw)
+                     static_cast<const char*>(vc), idx, row_len, k, out, lse, T, Hkv, kv_len, \
+                     L_cap, c_log2, sp.rows_per_split, partials, gpw)
     if (sp.waves_per_head == 4) CLSA_SPLIT_MFMA(4);
     else if (sp.waves_per_head == 2) CLSA_SPLIT_MFMA(2);
     else CLSA_SPLIT_MFMA(1);
@@ -692,8 +686,8 @@ int launch_index_path(const void* q, const void* kc, const void* vc, const int32
   } else {
     hipLaunchKernelGGL((attn_split_kernel<DT, G>), grid, block, 0, stream,
                        static_cast<const char*>(q), static_cast<const char*>(kc),
-                       static_cast<const char*>(vc), idx, k, out, lse, T, Hkv, kv_len, L_cap,
-                       c_log2, sp.rows_per_split, partials, gpw);
+                       static_cast<const char*>(vc), idx, row_len, k, out, lse, T, Hkv, kv_len,
+                       L_cap, c_log2, sp.rows_per_split, partials, gpw);
   }
   int rc = check_launch("attn_split");
   if (rc || sp.splits == 1) return rc;
@@ -704,13 +698,13 @@ int launch_index_path(const void* q, const void* kc, const void* vc, const int32
 
 template <int DT>
 int dispatch_index_path(int G, const void* q, const void* kc, const void* vc, const int32_t* idx,
-                        int k, void* out, float* lse, int B, int T, int Hkv, int kv_len, int L_cap,
+                        const int32_t* row_len, int k, void* out, float* lse, int B, int T, int Hkv, int kv_len, int L_cap,
                         float c_log2, const AttnSplit& sp, float* part, hipStream_t s) {
   switch (G) {
-    case 1: return launch_index_path<DT, 1>(q, kc, vc, idx, k, out, lse, B, T, Hkv, kv_len, L_cap, c_log2, sp, part, s);
-    case 2: return launch_index_path<DT, 2>(q, kc, vc, idx, k, out, lse, B, T, Hkv, kv_len, L_cap, c_log2, sp, part, s);
-    case 4: return launch_index_path<DT, 4>(q, kc, vc, idx, k, out, lse, B, T, Hkv, kv_len, L_cap, c_log2, sp, part, s);
-    case 8: return launch_index_path<DT, 8>(q, kc, vc, idx, k, out, lse, B, T, Hkv, kv_len, L_cap, c_log2, sp, part, s);
+    case 1: return launch_index_path<DT, 1>(q, kc, vc, idx, row_len, k, out, lse, B, T, Hkv, kv_len, L_cap, c_log2, sp, part, s);
+    case 2: return launch_index_path<DT, 2>(q, kc, vc, idx, row_len, k, out, lse, B, T, Hkv, kv_len, L_cap, c_log2, sp, part, s);
+    case 4: return launch_index_path<DT, 4>(q, kc, vc, idx, row_len, k, out, lse, B, T, Hkv, kv_len, L_cap, c_log2, sp, part, s);
+    case 8: return launch_index_path<DT, 8>(q, kc, vc, idx, row_len, k, out, lse, B, T, Hkv, kv_len, L_cap, c_log2, sp, part, s);
   }
   return set_error(CLSA_ERR_UNSUPPORTED, "sparse_attn: Hq/Hkv=%d", G);
 }
@@ -751,7 +745,6 @@ AttnSplit attn_split(int B, int T, int Hkv, int k, bool mfma) {
   int rows = (int)((k + s - 1) / s);
   rows = (rows + step * W - 1) / (step * W) * (step * W);
   L.waves_per_head = W;
-  L.skip_empty_steps = false;
   L.rows_per_split = rows;
   L.splits = (k + rows - 1) / rows;
   return L;
@@ -767,16 +760,15 @@ size_t attn_partial_floats(int B, int T, int Hq, int Hkv, int k) {
 
 int launch_sparse_attn(const void* q, const void* kc, const void* vc, int dtype, const int32_t* idx,
                        int k, void* out, float* lse, int B, int T, int Hq, int Hkv, int D,
-                       int kv_len, int L_cap, float scale, float* partials, bool skip_empty_steps,
-                       hipStream_t stream) {
-  AttnSplit sp = attn_split(B, T, Hkv, k, dtype == CLSA_BF16);
-  sp.skip_empty_steps = skip_empty_steps;
+                       int kv_len, int L_cap, float scale, float* partials,
+                       const int32_t* row_len, hipStream_t stream) {
+  const AttnSplit sp = attn_split(B, T, Hkv, k, dtype == CLSA_BF16);
   const float c_log2 = (scale > 0.f ? scale : 1.f / sqrtf((float)D)) * kLog2e;
   const int G = Hq / Hkv;
   if (dtype == CLSA_BF16)
-    return dispatch_index_path<CLSA_BF16>(G, q, kc, vc, idx, k, out, lse, B, T, Hkv, kv_len, L_cap,
+    return dispatch_index_path<CLSA_BF16>(G, q, kc, vc, idx, row_len, k, out, lse, B, T, Hkv, kv_len, L_cap,
                                           c_log2, sp, partials, stream);
-  return dispatch_index_path<CLSA_F32>(G, q, kc, vc, idx, k, out, lse, B, T, Hkv, kv_len, L_cap,
+  return dispatch_index_path<CLSA_F32>(G, q, kc, vc, idx, row_len, k, out, lse, B, T, Hkv, kv_len, L_cap,
                                        c_log2, sp, partials, stream);
 }
 
