@@ -5,6 +5,7 @@ anything (these calls never reach a HIP API, so no GPU is needed)."""
 import ctypes
 import os
 import re
+import subprocess
 
 import pytest
 
@@ -197,3 +198,40 @@ def test_step_descriptor_layout_matches_header(lib):
                          1, 1, 32, 8, 128, 64, 128, 100, 100, 16, 0.0, ctypes.POINTER(P)(), FAKE + 2)
     assert lib.clsa_decode_step(ctypes.byref(d), FAKE, 1 << 30, None) == -1
     assert b"k_per_query" in lib.clsa_last_error()
+
+
+def test_topk_margin_rejects(lib):
+    f = lib.clsa_topk_margin
+    assert f(FAKE, 1, 1, 100, 5, None, -1.0, FAKE, None, FAKE, 1 << 20, None) == -1
+    assert b"margin" in lib.clsa_last_error()
+    assert f(FAKE, 1, 1, 100, 5, None, float("nan"), FAKE, None, FAKE, 1 << 20, None) == -1
+    assert f(FAKE, 1, 1, 100, 5, None, 1.0, FAKE, FAKE + 2, FAKE, 1 << 20, None) == -1  # kept misaligned
+    assert f(FAKE, 1, 1, 100, 0, None, 1.0, FAKE, None, FAKE, 1 << 20, None) == -1      # k = 0
+    assert f(FAKE, 1, 1, 100, 5, None, 1.0, FAKE, None, FAKE, 16, None) == -3           # workspace
+
+
+def test_decode_step_rejects_negative_skip_margin(lib):
+    for bad in (-0.5, float("nan")):
+        m = ctypes.c_float(bad)
+        d = _desc([0, 0], skip_margin=ctypes.pointer(m))
+        assert lib.clsa_decode_step_workspace_bytes(ctypes.byref(d)) == 0
+        assert lib.clsa_decode_step(ctypes.byref(d), FAKE, 1 << 40, None) == -1
+        assert b"skip_margin" in lib.clsa_last_error()
+
+
+def test_step_desc_layout_matches_the_header(tmp_path):
+    # The binding's ctypes mirror of clsa_step_desc must have the C layout:
+    # compile a probe against include/clsa.h and compare every field offset.
+    fields = [name for name, _ in binding.StepDesc._fields_]
+    src = tmp_path / "probe.c"
+    src.write_text(
+        "#include <stdio.h>\n#include <stddef.h>\n#include \"clsa.h\"\nint main(void) {\n"
+        '  printf("size %zu\\n", sizeof(clsa_step_desc));\n'
+        + "".join(f'  printf("{n} %zu\\n", offsetof(clsa_step_desc, {n}));\n' for n in fields)
+        + "  return 0;\n}\n")
+    exe = tmp_path / "probe"
+    subprocess.check_call(["gcc", "-std=c11", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)])
+    out = dict(line.split() for line in subprocess.check_output([str(exe)]).decode().splitlines())
+    assert int(out["size"]) == ctypes.sizeof(binding.StepDesc)
+    for n in fields:
+        assert int(out[n]) == getattr(binding.StepDesc, n).offset, n
