@@ -110,6 +110,17 @@ TOPK_CASES = [
     ("sampled", 1, 1, 50001, 1000),
     ("needle", 2, 1, 131073, 2048),    # misaligned second row
     ("desc", 1, 1, 40000, 2048),       # the top k fill one 4096-chunk: its candidate segment overflows
+    # Short rows: one launch with the row in LDS (kv_len <= 8192, or <= 16384 with 8k >= kv_len).
+    ("ties", 3, 1, 8192, 700),         # giant tie classes
+    ("zeros", 2, 1, 8000, 300),        # all zeros, mixed signs
+    ("const", 1, 1, 6000, 2000),       # every key tied
+    ("relu", 2, 2, 7000, 999),         # causal rows, half exact zeros
+    ("needle", 4, 1, 8191, 64),        # odd length: rows after the first are misaligned
+    ("wide", 2, 1, 5000, 17),
+    ("desc", 1, 1, 8192, 2048),
+    ("sampled", 1, 1, 8192, 1000),
+    ("gauss", 2, 1, 12000, 2048),      # k >= kv_len / 8 up to 16384
+    ("ties", 1, 3, 16384, 2048),
 ]
 
 

@@ -41,6 +41,8 @@ def _margins(s, k):
     ("strided", 2, 1, 131072, 3000),   # full-row redo path
     ("desc", 2, 1, 40000, 2048),       # overflowing chunk path
     ("gauss", 2, 3, 700, 2048),        # k above the visible count
+    ("ties", 2, 1, 8000, 1000),        # short rows: one launch, row in LDS
+    ("gauss", 3, 2, 12000, 2048),
 ])
 def test_topk_margin_matches_oracle(kind, B, T, L, k):
     s = inp.score_rows(kind, B, T, L, 71, DEV)

@@ -6,7 +6,8 @@
 // padding when fewer than k positions are visible.
 //
 // Scores become order-preserving 32-bit keys (-0 folded onto +0); selection
-// is radix selection on digits of at most 12 bits. Two launches:
+// is radix selection on digits of at most 12 bits. Short rows take one
+// launch (topk_lds, below: the row is read into LDS once); longer rows two:
 //   1. topk_filter (chunks x rows, 256 threads): every workgroup of a row
 //      takes the same deterministic sample of the row (128 runs of 16
 //      consecutive elements, evenly spaced, so the sample costs 128 cache
@@ -55,6 +56,7 @@ constexpr int kSampleRun = 16;     // ... taken as kSample / kSampleRun evenly s
 constexpr int kTile = 16384;       // fallback tile: 16 waves x 1024 consecutive elements
 constexpr int kLdsCap = 12288;     // candidates kept in LDS
 constexpr int kHistCopies = 2;     // fallback histogram copies
+constexpr int kLdsRow = 16384;     // rows up to this length: one launch, row in LDS
 
 // Finds the bin b (scanning bins from high to low) where the running count
 // first reaches `need`; res[0] = b, res[1] = count in bins above b. Thread t
@@ -533,6 +535,50 @@ __global__ __launch_bounds__(kFilterThreads) void topk_filter(const float* __res
   }
 }
 
+// Row set-up shared by the select kernels: applies the row's own count
+// (k_rows: slots past it hold -1; k becomes the count) and handles rows that
+// keep every visible position (vis <= k: all of them in order, or with a
+// finite margin those scoring at least the row maximum minus the margin).
+// Returns true when the row is done (out and kept written). Uniform over the
+// workgroup; every thread must call it.
+__device__ bool row_prologue(const float* srow, int vis, int& k, const int32_t* k_rows, int row,
+                             float margin, int32_t* out, int32_t* kept_row,
+                             uint32_t (*mm)[kWaves], int* tmp) {
+  if (k_rows) {  // this row keeps kr positions; slots kr .. k-1 hold -1
+    const int kr = min(max(k_rows[row], 0), k);
+    for (int i = kr + threadIdx.x; i < k; i += kThreads) out[i] = -1;
+    k = kr;
+    if (k == 0) {
+      if (kept_row && threadIdx.x == 0) *kept_row = 0;
+      return true;
+    }
+  }
+  if (vis > k) return false;
+  if (!(margin < INFINITY)) {  // every visible position, in order
+    for (int i = threadIdx.x; i < k; i += kThreads) out[i] = i < vis ? i : -1;
+    if (kept_row && threadIdx.x == 0) *kept_row = vis;
+    return true;
+  }
+  // ... those at or above the threshold: row maximum, then an ordered
+  // compaction of the visible positions.
+  uint32_t mn = 0xffffffffu, mx = 0u;
+  for (int i = threadIdx.x; i < vis; i += kThreads) mx = max(mx, score_key(srow[i]));
+  block_minmax(mn, mx, mm);
+  const uint32_t mkey = margin_key(mx, margin);
+  int base = 0;
+  for (int t0 = 0; t0 < vis; t0 += kThreads) {  // uniform
+    const int i = t0 + threadIdx.x;
+    const int f = i < vis && score_key(srow[i]) >= mkey;
+    int tot;
+    const int pre = block_exclusive_scan<kThreads>(f, tmp, &tot);
+    if (f) out[base + pre] = i;
+    base += tot;
+  }
+  for (int i = base + threadIdx.x; i < k; i += kThreads) out[i] = -1;
+  if (kept_row && threadIdx.x == 0) *kept_row = base;
+  return true;
+}
+
 // grid (rows), block 1024.
 __global__ __launch_bounds__(kThreads) void topk_select(const float* __restrict__ scores,
                                                         const uint32_t* __restrict__ counts,
@@ -555,42 +601,9 @@ __global__ __launch_bounds__(kThreads) void topk_select(const float* __restrict_
   const int vis = kv_len - T + (row % T) + 1;
   int32_t* out = idx + (size_t)row * k;  // k slots
   int32_t* kept_row = kept ? kept + row : nullptr;
-  if (k_rows) {  // this row keeps kr positions; slots kr .. k-1 hold -1
-    const int kr = min(max(k_rows[row], 0), k);
-    for (int i = kr + threadIdx.x; i < k; i += kThreads) out[i] = -1;
-    k = kr;
-    if (k == 0) {
-      if (kept_row && threadIdx.x == 0) *kept_row = 0;
-      return;
-    }
-  }
   const float* srow = scores + (size_t)row * kv_len;
+  if (row_prologue(srow, vis, k, k_rows, row, margin, out, kept_row, mm, tmp)) return;
   const bool skip = margin < INFINITY;  // ordered skipping (uniform)
-  if (vis <= k) {  // every visible position, in order
-    if (!skip) {
-      for (int i = threadIdx.x; i < k; i += kThreads) out[i] = i < vis ? i : -1;
-      if (kept_row && threadIdx.x == 0) *kept_row = vis;
-      return;
-    }
-    // ... those at or above the threshold: row maximum, then an ordered
-    // compaction of the visible positions.
-    uint32_t mn = 0xffffffffu, mx = 0u;
-    for (int i = threadIdx.x; i < vis; i += kThreads) mx = max(mx, score_key(srow[i]));
-    block_minmax(mn, mx, mm);
-    const uint32_t mkey = margin_key(mx, margin);
-    int base = 0;
-    for (int t0 = 0; t0 < vis; t0 += kThreads) {  // uniform
-      const int i = t0 + threadIdx.x;
-      const int f = i < vis && score_key(srow[i]) >= mkey;
-      int tot;
-      const int pre = block_exclusive_scan<kThreads>(f, tmp, &tot);
-      if (f) out[base + pre] = i;
-      base += tot;
-    }
-    for (int i = base + threadIdx.x; i < k; i += kThreads) out[i] = -1;
-    if (kept_row && threadIdx.x == 0) *kept_row = base;
-    return;
-  }
   // Chunk owned by this thread for the gather: tpc threads per chunk, thread
   // j0 of a chunk takes entries j0, j0 + tpc, ... Its first kSpec entries are
   // loaded now, before the counts are known (the slots exist whatever the
@@ -675,6 +688,104 @@ __global__ __launch_bounds__(kThreads) void topk_select(const float* __restrict_
   select_and_emit(acc, n, k - above, b0 << 20, 1ull << 20, h, res, tmp, out, k, mkey, kept_row);
 }
 
+
+// A whole row held in LDS as keys.
+struct RowCand {
+  const uint32_t* key;
+  __device__ int p(int i) const { return i; }
+  __device__ uint32_t k(int i) const { return key[i]; }
+};
+
+// Loads the visible part of a row into LDS as keys; returns this thread's
+// min and max key through mn, mx.
+template <bool VEC>
+__device__ void load_row_keys(const float* srow, int vis, uint32_t* key, uint32_t& mn, uint32_t& mx) {
+  constexpr int kB = kLdsRow / (4 * kThreads);  // float4 loads per thread, all in flight
+  float x[kB][4];
+#pragma unroll
+  for (int u = 0; u < kB; u++) load4<VEC>(srow, 4 * threadIdx.x + u * 4 * kThreads, vis, x[u]);
+#pragma unroll
+  for (int u = 0; u < kB; u++)
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      const int e = 4 * threadIdx.x + u * 4 * kThreads + j;
+      if (e < vis) {
+        const uint32_t kk = score_key(x[u][j]);
+        key[e] = kk;
+        mn = min(mn, kk);
+        mx = max(mx, kk);
+      }
+    }
+}
+
+// Short rows (at most kLdsRow positions), in one launch (grid (rows), block
+// 1024): the row is read once into LDS as keys; a threshold from kSample
+// evenly spaced keys of it, binned over the sample's own range like the
+// filter's, is checked to leave at least k keys at or above it and then
+// bounds the radix selection from below, so its passes histogram only those
+// keys; the ordered emission scans the row in LDS. Same results as
+// topk_filter + topk_select.
+__global__ __launch_bounds__(kThreads) void topk_lds(const float* __restrict__ scores,
+                                                     int32_t* __restrict__ idx, int T, int kv_len,
+                                                     int k, const int32_t* __restrict__ k_rows,
+                                                     float margin, int32_t* __restrict__ kept) {
+  __shared__ __attribute__((aligned(16))) uint32_t key[kLdsRow];
+  __shared__ uint32_t h[kBins0];
+  __shared__ uint32_t mm[2][kWaves];
+  __shared__ uint32_t smm[2][kWaves];
+  __shared__ int tmp[17];
+  __shared__ int res[3];
+  const int row = blockIdx.x;
+  const int vis = kv_len - T + (row % T) + 1;
+  int32_t* out = idx + (size_t)row * k;
+  int32_t* kept_row = kept ? kept + row : nullptr;
+  const float* srow = scores + (size_t)row * kv_len;
+  if (row_prologue(srow, vis, k, k_rows, row, margin, out, kept_row, mm, tmp)) return;
+  uint32_t mn = 0xffffffffu, mx = 0u;
+  if ((reinterpret_cast<uintptr_t>(srow) & 15) == 0)
+    load_row_keys<true>(srow, vis, key, mn, mx);
+  else
+    load_row_keys<false>(srow, vis, key, mn, mx);
+  block_minmax(mn, mx, mm);  // its barrier also publishes the keys
+  // Sample: kSample keys at evenly spaced positions (vis > k >= 1 here).
+  const int m = min(kSample, vis);
+  constexpr int kPer = kSample / kThreads;
+  uint32_t sk[kPer];
+  uint32_t smn = 0xffffffffu, smx = 0u;
+#pragma unroll
+  for (int j = 0; j < kPer; j++) {
+    const int i = threadIdx.x + j * kThreads;
+    sk[j] = i < m ? key[(int)((long)i * vis / m)] : 0u;
+    if (i < m) {
+      smn = min(smn, sk[j]);
+      smx = max(smx, sk[j]);
+    }
+  }
+  for (int i = threadIdx.x; i < kBins0; i += kThreads) h[i] = 0u;
+  block_minmax(smn, smx, smm);  // its barrier also orders the clear before the counts
+  const uint64_t sspan = (uint64_t)(smx - smn) + 1;
+  const int bits = sspan == 1 ? 0 : 64 - __clzll(sspan - 1);
+  const int sh = bits > 12 ? bits - 12 : 0;
+  const int nb = 1 << (bits - sh);
+#pragma unroll
+  for (int j = 0; j < kPer; j++)
+    if (threadIdx.x + j * kThreads < m) atomicAdd(&h[(sk[j] - smn) >> sh], 1u);
+  __syncthreads();
+  const long expect = ((long)k * m + vis - 1) / vis;  // rank of the k-th key in the sample
+  find_bin<kThreads>(h, nb, (int)min((long)m, 2 * expect + 8), res, tmp);
+  uint32_t lo = smn + ((uint32_t)res[0] << sh);
+  // Keep the threshold only if at least k keys reach it (else the whole range).
+  int c = 0;
+  for (int e = threadIdx.x; e < vis; e += kThreads) c += key[e] >= lo;
+  int total;
+  block_exclusive_scan<kThreads>(c, tmp, &total);
+  if (total < k) lo = mn;
+  const uint64_t span = (uint64_t)(mx - lo) + 1;  // mx >= lo: the k-th key is at or above lo
+  const uint64_t R = span == 1 ? 1 : 1ull << (64 - __clzll(span - 1));
+  select_and_emit(RowCand{key}, vis, k, lo, R, h, res, tmp, out, k,
+                  margin < INFINITY ? margin_key(mx, margin) : 0u, kept_row);
+}
+
 }  // namespace
 
 int zero_words(uint32_t* p, size_t n, hipStream_t stream) {
@@ -701,6 +812,18 @@ int launch_topk(const float* scores, int B, int T, int kv_len, int k, const int3
   const TopkBuffers tb = topk_buffers(rows, kv_len);
   if (tb.nchunks > kTopkMaxChunks)
     return set_error(CLSA_ERR_UNSUPPORTED, "topk: kv_len=%d above %d", kv_len, kTopkMaxChunks * kChunk);
+  // One launch with the row in LDS for short rows: one CU reads a whole row,
+  // which pays off up to 8K positions (4096: 10.0 against 12.9 us for the
+  // two launches; 64 rows of 8192: 12.6 against 15.7 us), and up to 16K when
+  // k is at least 1/8 of the row (the filter's segments then overflow into
+  // the full-row redo: 2 rows of 12000, k = 2048: 13.9 against 22.5 us),
+  // but not for 16K rows with few candidates (4 rows, k = 1024: 19.1
+  // against 16.2 us) nor for longer rows (8 x 32768: 31.6 against 17.6 us).
+  if (kv_len <= kLdsRow / 2 || (kv_len <= kLdsRow && 8L * k >= kv_len)) {
+    hipLaunchKernelGGL(topk_lds, dim3(rows), dim3(kThreads), 0, stream, scores, idx, T, kv_len, k,
+                       k_rows, margin, kept);
+    return check_launch("topk_lds");
+  }
   int2* segs = reinterpret_cast<int2*>(cand);
   // Chunks per filter workgroup: one while the grid stays small (decode),
   // more when rows are many (a chunk's queries), so the row's threshold is
