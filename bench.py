@@ -7,7 +7,9 @@ N layers runs gathered sparse attention with that one index (CLSA: one
 indexer, N cross-decoder layers over one shared KV cache). Default workload:
 the 128K-context decode (B=4, kv_len=131072, 64x128 bf16 indexer, k=2048,
 16 layers, 32 q / 8 KV heads, dim 128, 1% needle keys), synthetic seeded
-inputs resident in HBM before the timed region starts.
+inputs resident in HBM before the timed region starts. Consecutive timed steps
+cycle through N_ROT sets of queries (same caches), so each step computes a new
+index, as consecutive decode steps do.
 
 Prints one JSON line: tokens/s for the step (K timed steps, nothing enqueued
 between them), the step's spread and its cold-cache time, and the roofline
@@ -36,6 +38,7 @@ import time
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 matrix cores
 MFMA_FP8_PEAK_TFLOPS = 5000.0    # MI355X dense fp8 matrix cores
+N_ROT = 4                        # query sets the timed steps cycle through
 ROOT = os.path.dirname(os.path.abspath(__file__))
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "sparse_attn_decode128k_traffic.txt")
 ATTN_SOURCE = os.path.join(ROOT, "token_sparse_attention_clsa_amd", "csrc", "sparse_attn.hip")
@@ -218,10 +221,31 @@ def main():
     X = inp.make(wl, args.variant, seed=7, device="cuda")
     n = wl.n_layers
     K, W = args.steps, args.warmup
-    step = clsa.DecodeStep(wl.layer_src, X.q, X.k_cache, X.v_cache, X.q_idx, X.k_idx, X.w, wl.k,
-                           kv_len=wl.kv_len)
-    for _ in range(W):
-        step.run()
+    # Consecutive decode steps see new queries, hence a new index each step:
+    # the timed steps cycle through N_ROT sets of attention and indexer
+    # queries (same caches), so a step's first layer does not find its rows
+    # in the caches from the step before, as it would if one step repeated.
+    qsets = [(X.q, X.q_idx, X.w)]
+    for r in range(1, N_ROT):
+        qsets.append(([inp.randn(t.shape, wl.dtype, 9000 + 97 * r + l, "cuda") for l, t in enumerate(X.q)],
+                      [None if t is None else inp.randn(t.shape, wl.idx_dtype, 9500 + 97 * r + l, "cuda")
+                       for l, t in enumerate(X.q_idx)],
+                      [None if t is None else inp.weights(t.shape, args.variant, 9900 + 97 * r + l, "cuda",
+                                                          bits=wl.weight_bits)
+                       for l, t in enumerate(X.w)]))
+    if args.variant == "int":  # integer indexer queries, as in the first set
+        qsets = qsets[:1] + [(q, [None if t is None else inp.randint(t.shape, -8, 8, wl.idx_dtype, 9700 + 97 * r + l,
+                                                                       "cuda")
+                                  for l, t in enumerate(qi)], w) for r, (q, qi, w) in enumerate(qsets[1:], 1)]
+
+    def make_steps(**kw):
+        return [clsa.DecodeStep(wl.layer_src, q, X.k_cache, X.v_cache, qi, X.k_idx, w, wl.k, kv_len=wl.kv_len, **kw)
+                for q, qi, w in qsets]
+
+    steps = make_steps()
+    step = steps[0]
+    for i in range(W):
+        steps[i % N_ROT].run()
     torch.cuda.synchronize()
     print(f"[bench] warmup done ({W} steps)", file=sys.stderr, flush=True)
 
@@ -230,8 +254,8 @@ def main():
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     e0.record()
-    for _ in range(K):
-        step.run()
+    for i in range(K):
+        steps[i % N_ROT].run()
     e1.record()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
@@ -240,27 +264,30 @@ def main():
     print(f"[bench] timed {K} steps: {ms_per_step * 1e3:.1f} us/step (events {ms_per_step_events * 1e3:.1f})",
           file=sys.stderr, flush=True)
 
-    # The same step captured once in a HIP graph and replayed K times (one
-    # launch per step instead of one per kernel; the work is identical).
+    # The N_ROT steps captured once in a HIP graph and replayed (one launch
+    # per N_ROT steps instead of one per kernel; the work is identical).
     graph_ms = None
     if not args.no_graph:
         g = torch.cuda.CUDAGraph()
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(side):
-            step.run()  # the step issues no allocations and no memset nodes
+            for st in steps:
+                st.run()  # the steps issue no allocations and no memset nodes
         torch.cuda.current_stream().wait_stream(side)
         torch.cuda.synchronize()
         with torch.cuda.graph(g):
-            step.run()
-        for _ in range(W):
+            for st in steps:
+                st.run()
+        reps = max(1, K // N_ROT)
+        for _ in range(max(1, W // N_ROT)):
             g.replay()
         torch.cuda.synchronize()
         t2 = time.perf_counter()
-        for _ in range(K):
+        for _ in range(reps):
             g.replay()
         torch.cuda.synchronize()
-        graph_ms = (time.perf_counter() - t2) * 1e3 / K
+        graph_ms = (time.perf_counter() - t2) * 1e3 / (reps * N_ROT)
         print(f"[bench] graph replay: {graph_ms * 1e3:.1f} us/step", file=sys.stderr, flush=True)
 
     # The same step with a per-query count of kept positions (the dynamic-k
@@ -270,15 +297,14 @@ def main():
     # the GPU starts, outside the steps themselves).
     gk = torch.Generator().manual_seed(17)
     kpq = torch.randint(wl.k // 4, wl.k + 1, (wl.B, wl.T), generator=gk, dtype=torch.int32).to("cuda")
-    step_dk = clsa.DecodeStep(wl.layer_src, X.q, X.k_cache, X.v_cache, X.q_idx, X.k_idx, X.w, wl.k,
-                              kv_len=wl.kv_len, k_per_query=kpq)
-    for _ in range(W):
-        step_dk.run()
+    step_dk = make_steps(k_per_query=kpq)
+    for i in range(W):
+        step_dk[i % N_ROT].run()
     torch.cuda.synchronize()
     e3a, e3b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e3a.record()
-    for _ in range(K):
-        step_dk.run()
+    for i in range(K):
+        step_dk[i % N_ROT].run()
     e3b.record()
     torch.cuda.synchronize()
     dynamic_k = {"k_per_query": f"uniform [{wl.k // 4}, {wl.k}]", "mean_k": float(kpq.float().mean()),
@@ -294,15 +320,14 @@ def main():
     margin = float((top[:, 0] - top[:, top.shape[1] // 2 - 1]).median())
     _, kept = clsa.topk_margin(sc, wl.k, margin)
     del sc, top
-    step_os = clsa.DecodeStep(wl.layer_src, X.q, X.k_cache, X.v_cache, X.q_idx, X.k_idx, X.w, wl.k,
-                              kv_len=wl.kv_len, skip_margin=margin)
-    for _ in range(W):
-        step_os.run()
+    step_os = make_steps(skip_margin=margin)
+    for i in range(W):
+        step_os[i % N_ROT].run()
     torch.cuda.synchronize()
     e4a, e4b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e4a.record()
-    for _ in range(K):
-        step_os.run()
+    for i in range(K):
+        step_os[i % N_ROT].run()
     e4b.record()
     torch.cuda.synchronize()
     ordered_skip = {"margin": margin, "rule": "median query keeps ~k/2 of its top-k",
@@ -423,7 +448,7 @@ def main():
     torch.cuda.synchronize()
     evs[0].record()
     for i in range(K):
-        step.run()
+        steps[i % N_ROT].run()
         evs[i + 1].record()
     torch.cuda.synchronize()
     per_step = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(K))
@@ -542,6 +567,7 @@ def main():
                         f"{inp.DTYPE_NAME[wl.idx_dtype]}, top-k {wl.k}, {n} layers sharing one index "
                         f"({len(f_layers)} indexer pass), GQA {wl.Hq}q/{wl.Hkv}kv x {wl.D}",
             "variant": args.variant,
+            "query_sets": N_ROT,
             "global_batch": wl.B,
             "seq_len": wl.kv_len,
             "parallelism": "single GPU",
