@@ -580,6 +580,7 @@ def main():
             "topk": us_topk,
             "cache_append": us_append,
             "index_score_gbs": alg["index_score"] / (us_index * 1e-6) / 1e9,
+            "topk_gbs": alg["topk"] / (us_topk * 1e-6) / 1e9,
         },
         "ms_per_step_events": ms_per_step_events,
         "ms_per_step_p10_p50_p90": [pct(0.1), pct(0.5), pct(0.9)],
