@@ -697,25 +697,25 @@ struct RowCand {
 };
 
 // Loads the visible part of a row into LDS as keys; returns this thread's
-// min and max key through mn, mx.
-template <bool VEC>
+// min and max key through mn, mx. Thread t takes elements t, t + 1024, ...
+// (coalesced); every load is issued unconditionally from a clamped address
+// and masked at use, so all of them are in flight together (conditional
+// loads make the compiler wait for each one before the next).
 __device__ void load_row_keys(const float* srow, int vis, uint32_t* key, uint32_t& mn, uint32_t& mx) {
-  constexpr int kB = kLdsRow / (4 * kThreads);  // float4 loads per thread, all in flight
-  float x[kB][4];
+  constexpr int kB = kLdsRow / kThreads;
+  float x[kB];
 #pragma unroll
-  for (int u = 0; u < kB; u++) load4<VEC>(srow, 4 * threadIdx.x + u * 4 * kThreads, vis, x[u]);
+  for (int u = 0; u < kB; u++) x[u] = srow[min((int)threadIdx.x + u * kThreads, vis - 1)];
 #pragma unroll
-  for (int u = 0; u < kB; u++)
-#pragma unroll
-    for (int j = 0; j < 4; j++) {
-      const int e = 4 * threadIdx.x + u * 4 * kThreads + j;
-      if (e < vis) {
-        const uint32_t kk = score_key(x[u][j]);
-        key[e] = kk;
-        mn = min(mn, kk);
-        mx = max(mx, kk);
-      }
+  for (int u = 0; u < kB; u++) {
+    const int e = threadIdx.x + u * kThreads;
+    if (e < vis) {
+      const uint32_t kk = score_key(x[u]);
+      key[e] = kk;
+      mn = min(mn, kk);
+      mx = max(mx, kk);
     }
+  }
 }
 
 // Short rows (at most kLdsRow positions), in one launch (grid (rows), block
@@ -742,10 +742,7 @@ __global__ __launch_bounds__(kThreads) void topk_lds(const float* __restrict__ s
   const float* srow = scores + (size_t)row * kv_len;
   if (row_prologue(srow, vis, k, k_rows, row, margin, out, kept_row, mm, tmp)) return;
   uint32_t mn = 0xffffffffu, mx = 0u;
-  if ((reinterpret_cast<uintptr_t>(srow) & 15) == 0)
-    load_row_keys<true>(srow, vis, key, mn, mx);
-  else
-    load_row_keys<false>(srow, vis, key, mn, mx);
+  load_row_keys(srow, vis, key, mn, mx);
   block_minmax(mn, mx, mm);  // its barrier also publishes the keys
   // Sample: kSample keys at evenly spaced positions (vis > k >= 1 here).
   const int m = min(kSample, vis);
