@@ -8,10 +8,12 @@
 // reuses the one index).
 //
 // Work split (index path): one workgroup per (query, split of the k
-// entries, block of KV heads), one wave per KV head, so the waves of a
-// workgroup read the same tokens' K/V rows (contiguous across KV heads in the
-// token-major cache) at about the same time, and each row leaves HBM once per
-// layer for all G query heads of its KV head.
+// entries, block of KV heads), W waves per KV head (W = 1, 2 or 4: see
+// attn_split). With one wave per head the waves of a workgroup read the same
+// tokens' K/V rows (contiguous across KV heads in the token-major cache) at
+// about the same time; in every plan each row leaves HBM once per layer for
+// all G query heads of its KV head. With per-row entry counts (row_len) a
+// row's entries past its count are neither read nor gathered.
 //  - bf16 (attn_split_mfma): q.K and P.V on matrix cores, 32 entries per
 //    step; described above the kernel.
 //  - fp32 (attn_split_kernel): the split's entries are staged in LDS; a row
