@@ -31,8 +31,9 @@ class _Ref:
     """Oracle results per sampled query, with host copies and indices memoised
     (layers share caches and F layers' indices)."""
 
-    def __init__(self, wl, X):
+    def __init__(self, wl, X, k_rows=None, margin=None):
         self.wl, self.X = wl, X
+        self.k_rows, self.margin = k_rows, margin  # per-query counts [B, T], ordered-skipping margin
         self._raw, self._idx = {}, {}
 
     def host(self, t, b):
@@ -47,7 +48,11 @@ class _Ref:
             vis = wl.kv_len - wl.T + t + 1
             scores = oracle.index_score(raw(X.q_idx[f][b:b + 1, t:t + 1]), self.host(X.k_idx[f], b),
                                         wl.idx_dtype, raw(X.w[f][b:b + 1, t:t + 1]), vis)
-            self._idx[(f, b, t)] = oracle.topk(scores, wl.k)
+            kr = None if self.k_rows is None else self.k_rows[b:b + 1, t:t + 1]
+            if self.margin is None:
+                self._idx[(f, b, t)] = oracle.topk(scores, wl.k, k_rows=kr)
+            else:
+                self._idx[(f, b, t)] = oracle.topk_margin(scores, wl.k, self.margin, k_rows=kr)[0]
         return self._idx[(f, b, t)]
 
     def unit(self, layer, b, t):
@@ -85,6 +90,28 @@ def test_decode128k_full_step():
     # the needles (keys x4) dominate the selection
     needles = set(X.needles[0].tolist())
     assert len(needles & set(st.idx[0, 0].tolist())) > 0.5 * len(needles)
+
+
+def test_decode128k_full_step_with_counts_and_margin():
+    # The benchmark's per-query-k and ordered-skipping configurations together:
+    # counts uniform in [k/4, k] and a margin at which the median query of
+    # batch element 0 keeps about half of its k positions (both rules apply).
+    wl = inp.config("decode128k")
+    announce("full decode128k, k_per_query + skip_margin", wl.B, wl.kv_len, wl.n_layers)
+    X = inp.make(wl, "int", seed=16, device=DEV)
+    kr = np.random.default_rng(17).integers(wl.k // 4, wl.k + 1, (wl.B, wl.T)).astype(np.int32)
+    s0 = oracle.index_score(raw(X.q_idx[0][0:1]), raw(X.k_idx[0][0:1]), wl.idx_dtype, raw(X.w[0][0:1]),
+                            wl.kv_len)
+    top = np.sort(s0[0, 0])[::-1]
+    margin = float(np.float32(top[0] - top[wl.k // 2 - 1]))
+    st = clsa.DecodeStep(wl.layer_src, X.q, X.k_cache, X.v_cache, X.q_idx, X.k_idx, X.w, wl.k,
+                         kv_len=wl.kv_len, k_per_query=torch.from_numpy(kr).to(DEV), skip_margin=margin)
+    st.run()
+    torch.cuda.synchronize()
+    ref = _Ref(wl, X, k_rows=kr, margin=margin)
+    _check_units(wl, X, st, [(l, b, 0) for b in range(wl.B) for l in (0, 7, 15)], ref)
+    kept = (st.idx.cpu().numpy() >= 0).sum(-1)
+    assert np.all(kept <= kr) and kept.min() < wl.k // 2  # counts and margin both cut
 
 
 def test_decode32k_full_step_bf16_and_fp8_indexer():
