@@ -518,7 +518,10 @@ def main():
     else:
         attn_tflops = 4.0 * wl.B * wl.T * wl.k * wl.Hq * wl.D / (us_attn * 1e-6) / 1e12
         attn_roof = {"bound": "mfma", "achieved": attn_tflops, "peak": MFMA_BF16_PEAK_TFLOPS,
-                     "unit": "TFLOP/s", "frac": attn_tflops / MFMA_BF16_PEAK_TFLOPS, "traffic": None}
+                     "unit": "TFLOP/s", "frac": attn_tflops / MFMA_BF16_PEAK_TFLOPS, "traffic": None,
+                     # the rate at which the call gathers its rows through the L2s (their
+                     # repeats across queries come from L2 / Infinity Cache, not HBM)
+                     "l2_gather_gbs": attn_gbs}
     split_kernel = "attn_split_mfma" if wl.dtype == 1 else "attn_split_kernel"
     attn_roof.update({"kernel": f"sparse_attn call ({split_kernel} + attn_combine_kernel)",
                       "bytes_per_launch": alg["sparse_attn"], "avg_launch_us": us_attn,
