@@ -89,6 +89,42 @@ def test_topk_margin_with_per_query_counts_matches_oracle():
         assert np.array_equal(kept.cpu().numpy(), ref_kept)
 
 
+def test_topk_margin_threshold_on_a_score_is_inclusive():
+    # Integer scores with integer margins: thr = max - margin is itself a
+    # score of the row, and entries equal to it are kept on both sides.
+    s = inp.score_rows("ties", 3, 2, 30000, 75, DEV)  # integers 0..7
+    s64 = s.double().cpu().numpy()
+    for margin in (1.0, 2.0, 3.0):
+        announce("topk_margin exact threshold", margin)
+        idx, kept = clsa.topk_margin(s, 2048, margin)
+        torch.cuda.synchronize()
+        ref_idx, ref_kept = oracle.topk_margin(s64, 2048, margin)
+        assert np.array_equal(idx.cpu().numpy(), ref_idx) and np.array_equal(kept.cpu().numpy(), ref_kept)
+
+
+def test_decode_step_fp32_with_skip_margin_matches_oracle():
+    # The fp32 attention kernel's per-row entry counts (tiny fp32 workload).
+    announce("decode step fp32 with skip_margin")
+    wl = inp.config("tiny")
+    X = inp.make(wl, "int", seed=8, device=DEV)
+    sc = oracle.index_score(raw(X.q_idx[0]), raw(X.k_idx[0]), wl.idx_dtype, raw(X.w[0]), wl.kv_len)
+    margin = _margins(sc, wl.k)[2]
+    st = clsa.DecodeStep(wl.layer_src, X.q, X.k_cache, X.v_cache, X.q_idx, X.k_idx, X.w, wl.k,
+                         kv_len=wl.kv_len, skip_margin=margin)
+    st.run()
+    torch.cuda.synchronize()
+    outs, lses, idx, _ = oracle.decode_step(
+        wl.layer_src, [raw(t) for t in X.q], [raw(t) for t in X.k_cache], [raw(t) for t in X.v_cache],
+        wl.dtype, [None if t is None else raw(t) for t in X.q_idx],
+        [None if t is None else raw(t) for t in X.k_idx], [None if t is None else raw(t) for t in X.w],
+        wl.idx_dtype, wl.kv_len, wl.k, skip_margin=margin)
+    assert (idx >= 0).sum(-1).min() < wl.k
+    assert np.array_equal(st.idx.cpu().numpy(), idx)
+    for l in range(wl.n_layers):
+        assert max_abs(out_f64(st.out[l]), outs[l]) <= TOL_OUT[wl.dtype]
+        lse_close(st.lse[l].cpu().numpy(), lses[l], TOL_LSE[wl.dtype])
+
+
 def test_topk_margin_rejects_negative_or_nan():
     s = torch.zeros((1, 1, 64), device=DEV)
     for bad in (-1.0, float("nan")):
