@@ -8,3 +8,13 @@ if ROOT not in sys.path:
 
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
+
+
+def pytest_terminal_summary(terminalreporter):
+    """Observed attention errors against their tolerances (GPU parity runs)."""
+    gu = sys.modules.get("gpu_util")
+    if gu is None or not getattr(gu, "OBSERVED", None):
+        return
+    terminalreporter.write_sep("-", "attention outputs: largest max-abs error per test (tolerance)")
+    for test, (err, tol) in sorted(gu.OBSERVED.items()):
+        terminalreporter.write_line(f"{err:10.3e}  ({tol:g}, {100.0 * err / tol:5.1f}% used)  {test}")

@@ -11,7 +11,7 @@ import oracle
 import token_sparse_attention_clsa_amd as clsa
 from token_sparse_attention_clsa_amd import inputs as inp
 
-from gpu_util import DEV, TOL_LSE, TOL_OUT, announce, lse_close, max_abs, out_f64, raw, require_gpu
+from gpu_util import DEV, TOL_LSE, TOL_OUT, announce, check_out, lse_close, max_abs, out_f64, raw, require_gpu
 
 pytestmark = pytest.mark.gpu
 
@@ -73,5 +73,5 @@ def test_decode_step_over_appended_token_matches_oracle():
     outs, lses, idx, _ = ref
     assert np.array_equal(st.idx.cpu().numpy(), idx)
     for l in range(wl.n_layers):
-        assert max_abs(out_f64(st.out[l]), outs[l]) <= TOL_OUT[wl.dtype]
+        check_out(out_f64(st.out[l]), outs[l], TOL_OUT[wl.dtype], f"layer {l}")
         lse_close(st.lse[l].cpu().numpy(), lses[l], TOL_LSE[wl.dtype])

@@ -10,7 +10,7 @@ import oracle
 import token_sparse_attention_clsa_amd as clsa
 from token_sparse_attention_clsa_amd import inputs as inp
 
-from gpu_util import DEV, TOL_LSE, TOL_OUT, announce, lse_close, max_abs, out_f64, raw, require_gpu
+from gpu_util import DEV, TOL_LSE, TOL_OUT, announce, check_out, lse_close, max_abs, out_f64, raw, require_gpu
 
 pytestmark = pytest.mark.gpu
 
@@ -62,7 +62,7 @@ def test_block_paged_attention_matches_oracle(B, T, L, k, block, Hq, Hkv):
     torch.cuda.synchronize()
     r_ptr, r_ind = oracle.block_union(idx.numpy(), L, block, Hkv)
     ref_o, ref_l = oracle.block_attn(raw(q), raw(kc), raw(vc), inp.BF16, r_ptr, r_ind, block, L)
-    assert max_abs(out_f64(out), ref_o) <= TOL_OUT[inp.BF16]
+    check_out(out_f64(out), ref_o, TOL_OUT[inp.BF16])
     lse_close(lse.cpu().numpy(), ref_l, TOL_LSE[inp.BF16])
 
 
@@ -85,5 +85,5 @@ def test_block_paged_attention_head_major_matches_oracle(B, T, L, k, block, Hq, 
     torch.cuda.synchronize()
     r_ptr, r_ind = oracle.block_union(idx.numpy(), L, block, Hkv)
     ref_o, ref_l = oracle.block_attn(raw(q), raw(kh), raw(vh), inp.BF16, r_ptr, r_ind, block, L, head_major=True)
-    assert max_abs(out_f64(out), ref_o) <= TOL_OUT[inp.BF16]
+    check_out(out_f64(out), ref_o, TOL_OUT[inp.BF16])
     lse_close(lse.cpu().numpy(), ref_l, TOL_LSE[inp.BF16])

@@ -18,7 +18,7 @@ import oracle
 import token_sparse_attention_clsa_amd as clsa
 from token_sparse_attention_clsa_amd import inputs as inp
 
-from gpu_util import DEV, TOL_LSE, TOL_OUT, announce, lse_close, max_abs, out_f64, raw, require_gpu
+from gpu_util import DEV, TOL_LSE, TOL_OUT, announce, check_out, lse_close, max_abs, out_f64, raw, require_gpu
 
 pytestmark = pytest.mark.gpu
 
@@ -66,7 +66,7 @@ def test_decode_step_integer_index_matches_oracle(name, over):
     assert calls == len(wl.f_layers)
     assert np.array_equal(st.idx.cpu().numpy(), idx)
     for l in range(wl.n_layers):
-        assert max_abs(out_f64(st.out[l]), outs[l]) <= TOL_OUT[wl.dtype], f"layer {l}"
+        check_out(out_f64(st.out[l]), outs[l], TOL_OUT[wl.dtype], f"layer {l}")
         lse_close(st.lse[l].cpu().numpy(), lses[l], TOL_LSE[wl.dtype])
 
 
@@ -81,7 +81,11 @@ def test_decode_step_gaussian_selection_within_rounding_bound():
     eps = 2.0 ** -16 * bound  # float32 rounding bound of each GPU score
     same_rows = []
     for b in range(wl.B):
-        g, r = set(got[b, 0].tolist()), set(ref_idx[b, 0].tolist())
+        row = got[b, 0]
+        # a valid index row first: k visible positions, strictly ascending
+        assert np.all(row >= 0) and np.all(row < wl.kv_len), b
+        assert np.all(np.diff(row) > 0), b
+        g, r = set(row.tolist()), set(ref_idx[b, 0].tolist())
         assert len(g) == wl.k
         theta = ref[b, 0, ref_idx[b, 0]].min()
         # a disagreement is allowed only where rounding can reorder a position
@@ -95,7 +99,7 @@ def test_decode_step_gaussian_selection_within_rounding_bound():
     assert same_rows, "no row selected the same positions"
     for l in range(wl.n_layers):
         for b in same_rows:
-            assert max_abs(out_f64(st.out[l][b]), outs[l][b]) <= TOL_OUT[wl.dtype]
+            check_out(out_f64(st.out[l][b]), outs[l][b], TOL_OUT[wl.dtype], f"layer {l} row {b}")
             lse_close(st.lse[l][b].cpu().numpy(), lses[l][b], TOL_LSE[wl.dtype])
 
 

@@ -12,7 +12,7 @@ import oracle
 import token_sparse_attention_clsa_amd as clsa
 from token_sparse_attention_clsa_amd import inputs as inp
 
-from gpu_util import DEV, TOL_LSE, TOL_OUT, announce, lse_close, max_abs, out_f64, raw, require_gpu
+from gpu_util import DEV, TOL_LSE, TOL_OUT, announce, check_out, lse_close, max_abs, out_f64, raw, require_gpu
 
 pytestmark = pytest.mark.gpu
 
@@ -66,5 +66,5 @@ def test_decode_step_with_per_query_counts_matches_oracle():
     assert np.array_equal(st.idx.cpu().numpy(), idx)
     assert np.all(idx[1, 0, 300:] == -1) and np.all(idx[2, 0, 1:] == -1)
     for l in range(wl.n_layers):
-        assert max_abs(out_f64(st.out[l]), outs[l]) <= TOL_OUT[wl.dtype]
+        check_out(out_f64(st.out[l]), outs[l], TOL_OUT[wl.dtype], f"layer {l}")
         lse_close(st.lse[l].cpu().numpy(), lses[l], TOL_LSE[wl.dtype])

@@ -17,7 +17,8 @@ import oracle
 import token_sparse_attention_clsa_amd as clsa
 from token_sparse_attention_clsa_amd import inputs as inp
 
-from gpu_util import DEV, TOL_LSE, TOL_OUT, announce, lse_close, max_abs, out_f64, raw, require_gpu
+from gpu_util import (DEV, TOL_LSE, TOL_OUT, announce, check_out, lse_close, oracle_index_rows, oracle_topk_rows,
+                      out_f64, raw, require_gpu)
 
 pytestmark = pytest.mark.gpu
 
@@ -71,7 +72,7 @@ def _check_units(wl, X, st, units, ref=None):
         idx, out, lse = ref.unit(layer, b, t)
         if wl.layer_src[layer] == wl.f_layers[-1]:  # the index cache holds the last F layer's index
             assert np.array_equal(st.idx[b, t].cpu().numpy(), idx), (layer, b, t)
-        assert max_abs(out_f64(st.out[layer][b, t]), out) <= TOL_OUT[wl.dtype], (layer, b, t)
+        check_out(out_f64(st.out[layer][b, t]), out, TOL_OUT[wl.dtype], str((layer, b, t)))
         lse_close(st.lse[layer][b, t].cpu().numpy(), lse, TOL_LSE[wl.dtype])
     return ref
 
@@ -112,6 +113,36 @@ def test_decode128k_full_step_with_counts_and_margin():
     _check_units(wl, X, st, [(l, b, 0) for b in range(wl.B) for l in (0, 7, 15)], ref)
     kept = (st.idx.cpu().numpy() >= 0).sum(-1)
     assert np.all(kept <= kr) and kept.min() < wl.k // 2  # counts and margin both cut
+
+
+def test_decode128k_gaussian_bench_inputs():
+    # The benchmark's own inputs (Gaussian recipe, seed 7): every indexer score
+    # within the float32 rounding bound of the oracle's, every index row equal
+    # to the oracle's top-k of the GPU's scores, and attention of the first and
+    # last layer for every batch element against the oracle fed that index.
+    wl = inp.config("decode128k")
+    announce("full decode128k gauss (bench inputs)", wl.B, wl.kv_len, wl.n_layers)
+    X = inp.make(wl, "gauss", seed=7, device=DEV)
+    st = clsa.DecodeStep(wl.layer_src, X.q, X.k_cache, X.v_cache, X.q_idx, X.k_idx, X.w, wl.k,
+                         kv_len=wl.kv_len)
+    st.run()
+    sc = clsa.index_score(X.q_idx[0], X.k_idx[0], X.w[0], kv_len=wl.kv_len)
+    torch.cuda.synchronize()
+    got = sc.cpu().numpy().astype(np.float64)
+    ref, bound = oracle_index_rows(raw(X.q_idx[0]), raw(X.k_idx[0]), wl.idx_dtype, raw(X.w[0]), wl.kv_len,
+                                   with_bound=True)
+    assert np.all(np.isfinite(got)) and np.all(np.isfinite(ref))
+    # float32 dot of <= 128 exact products plus a 64-term head sum: |err| <= 2^-16 * bound
+    assert np.all(np.abs(got - ref) <= 2.0 ** -16 * bound + 1e-30)
+    idx = st.idx.cpu().numpy()
+    assert np.array_equal(idx, oracle_topk_rows(got, wl.k))
+    ref_x = _Ref(wl, X)
+    for layer in (0, wl.n_layers - 1):
+        for b in range(wl.B):
+            out, lse = oracle.sparse_attn(raw(X.q[layer][b:b + 1]), ref_x.host(X.k_cache[layer], b),
+                                          ref_x.host(X.v_cache[layer], b), wl.dtype, idx[b:b + 1], wl.kv_len)
+            check_out(out_f64(st.out[layer][b]), out[0], TOL_OUT[wl.dtype], str((layer, b)))
+            lse_close(st.lse[layer][b].cpu().numpy(), lse[0], TOL_LSE[wl.dtype])
 
 
 def test_decode32k_full_step_bf16_and_fp8_indexer():
@@ -160,6 +191,19 @@ def test_prefill2k_full_chunk():
     vis = wl.kv_len - wl.T + np.arange(wl.T) + 1
     assert np.all(idx < vis[:, None])
     assert np.all(idx >= 0)  # every query sees more than k positions
+    # Every query's index row: the GPU's own integer-recipe scores (exact in
+    # any summation order; sampled rows are checked against the oracle's
+    # scores here too) through the oracle's top-k. This covers the top-k
+    # filter's several-chunks-per-workgroup mode on all 2048 rows.
+    sc = clsa.index_score(X.q_idx[0], X.k_idx[0], X.w[0], kv_len=wl.kv_len)
+    torch.cuda.synchronize()
+    got = sc.cpu().numpy()
+    del sc
+    for t in (0, 1024, 2047):
+        ref_t = oracle.index_score(raw(X.q_idx[0][:, t:t + 1]), raw(X.k_idx[0]), wl.idx_dtype,
+                                   raw(X.w[0][:, t:t + 1]), wl.kv_len - wl.T + t + 1)
+        assert np.array_equal(got[0, t, :wl.kv_len - wl.T + t + 1].astype(np.float64), ref_t[0, 0])
+    assert np.array_equal(idx, oracle_topk_rows(got, wl.k)[0])
 
 
 def test_topk_at_maximum_row_length():

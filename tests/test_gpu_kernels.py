@@ -19,7 +19,8 @@ import oracle
 import token_sparse_attention_clsa_amd as clsa
 from token_sparse_attention_clsa_amd import inputs as inp
 
-from gpu_util import DEV, TOL_LSE, TOL_OUT, announce, lse_close, max_abs, out_f64, raw, require_gpu
+from gpu_util import (DEV, TOL_LSE, TOL_OUT, announce, check_out, lse_close, oracle_attn_rows, oracle_topk_rows,
+                      out_f64, raw, require_gpu)
 
 pytestmark = pytest.mark.gpu
 
@@ -121,6 +122,11 @@ TOPK_CASES = [
     ("sampled", 1, 1, 8192, 1000),
     ("gauss", 2, 1, 12000, 2048),      # k >= kv_len / 8 up to 16384
     ("ties", 1, 3, 16384, 2048),
+    # Many long causal rows (a chunk's queries): the filter takes several
+    # chunks per workgroup under one threshold (rows x chunks >= 16384).
+    ("gauss", 1, 1024, 65536, 2048),   # 2 chunks per filter workgroup
+    ("ties", 1, 512, 131072, 2048),    # 2 chunks per workgroup, giant tie classes
+    ("needle", 2, 600, 66000, 1000),   # 2 chunks per workgroup, a ragged last chunk
 ]
 
 
@@ -130,7 +136,7 @@ def test_topk_bit_exact(kind, B, T, L, k):
     s = inp.score_rows(kind, B, T, L, 31, DEV)
     idx = clsa.topk(s, k)
     torch.cuda.synchronize()
-    ref = oracle.topk(s.double().cpu().numpy(), k)
+    ref = oracle_topk_rows(s.cpu().numpy(), k)
     assert np.array_equal(idx.cpu().numpy(), ref)
 
 
@@ -159,6 +165,10 @@ ATTN_CASES = [
     (inp.BF16, 1, 2, 32, 4, 4096, 4096, 4096),
     (inp.BF16, 1, 4, 16, 2, 900, 900, 33),
     (inp.F32, 2, 2, 8, 4, 1000, 1024, 100),
+    # B*T*Hkv >= 2048: one wave per (query, KV head) walks the whole row, no
+    # split states (the chunked-prefill plan): 64 and 128 steps of 32 entries
+    (inp.BF16, 1, 256, 32, 8, 8192, 8192, 2048),
+    (inp.BF16, 1, 300, 32, 8, 9000, 9100, 4096),
 ]
 
 
@@ -185,8 +195,8 @@ def test_sparse_attn_matches_oracle(dt, B, T, Hq, Hkv, L, cap, k):
     idx = _index(B, T, L, k, 44).to(DEV)
     out, lse = clsa.sparse_attn(q, kc, vc, idx, kv_len=L)
     torch.cuda.synchronize()
-    ref_o, ref_l = oracle.sparse_attn(raw(q), raw(kc), raw(vc), dt, raw(idx), L)
-    assert max_abs(out_f64(out), ref_o) <= TOL_OUT[dt]
+    ref_o, ref_l = oracle_attn_rows(raw(q), raw(kc), raw(vc), dt, raw(idx), L)
+    check_out(out_f64(out), ref_o, TOL_OUT[dt])
     lse_close(lse.cpu().numpy(), ref_l, TOL_LSE[dt])
 
 
