@@ -33,7 +33,9 @@
  *  - GQA: query head h reads KV head g = h / (Hq / Hkv).
  *  - Ownership: the caller allocates and frees every buffer, including the
  *    workspace. The library allocates no device memory and keeps no device
- *    state between calls. Host arrays are only read during the call.
+ *    state between calls (one exception: the scratch array behind
+ *    clsa_decode_step_static, which the library holds on each GPU). Host
+ *    arrays are only read during the call.
  *  - Asynchrony: every call enqueues its kernels on `stream` (a hipStream_t;
  *    NULL means the default stream) and returns without synchronising.
  *  - Errors: all arguments are validated before the first launch, so a call
@@ -248,6 +250,23 @@ size_t clsa_decode_step_workspace_bytes(const clsa_step_desc* d);
 
 int clsa_decode_step(const clsa_step_desc* d, void* ws, size_t ws_bytes,
                      void* stream);
+
+/*
+ * clsa_decode_step without a workspace argument, for callers that cannot
+ * allocate device memory: work recorded under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation. The step's scratch (the
+ * bytes clsa_decode_step_workspace_bytes(d) reports) lives in a device array
+ * of CLSA_STATIC_SCRATCH_BYTES that the library holds on each GPU it runs on
+ * until the process ends; the call allocates nothing. A step needing more
+ * returns CLSA_ERR_WORKSPACE before launching anything (at the 128K-context
+ * decode, B = 4, it needs about 6 MiB; a 2048-query chunk's scores alone are
+ * about 1 GiB and do not fit). Every call on one GPU uses that GPU's array:
+ * calls that overlap in time on one GPU (several streams or threads) race on
+ * it and must be serialised by the caller. Results, errors and the
+ * descriptor are as for clsa_decode_step on the current device.
+ */
+#define CLSA_STATIC_SCRATCH_BYTES ((size_t)64 << 20)
+int clsa_decode_step_static(const clsa_step_desc* d, void* stream);
 
 /*
  * Block-union KV table (CompactAttention summary, "Méthodologie", selection

@@ -34,7 +34,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = clsa.declared_symbols()
-    assert len(names) == 15
+    assert len(names) == 16
     for required in ("clsa_index_score", "clsa_topk", "clsa_topk_margin", "clsa_sparse_attn",
                      "clsa_decode_step"):
         assert required in names
@@ -245,3 +245,18 @@ def test_step_desc_layout_matches_the_header(tmp_path):
     for n in fields:
         assert int(out[n]) == getattr(binding.StepDesc, n).offset, n
 
+
+def test_decode_step_static_rejects(lib):
+    # an invalid layer map: the regular step's message, nothing launched
+    d = _desc([1, 1])
+    assert lib.clsa_decode_step_static(ctypes.byref(d), None) == -1
+    assert b"layer" in lib.clsa_last_error()
+    # a step whose scratch exceeds the library's array
+    big = _desc([0, 0], B=8, kv_len=4_000_000, L_cap=4_000_000)
+    need = lib.clsa_decode_step_workspace_bytes(ctypes.byref(big))
+    text = open(os.path.join(ROOT, "include", "clsa.h")).read()
+    cap = eval(re.search(r"#define CLSA_STATIC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", text)
+               .expand(r"\1 << \2"))
+    assert need > cap
+    assert lib.clsa_decode_step_static(ctypes.byref(big), None) == -3
+    assert b"scratch" in lib.clsa_last_error()

@@ -84,6 +84,7 @@ def load() -> ctypes.CDLL:
         "clsa_sparse_attn": (I, [P, P, P, I, P, I, P, P] + [I] * 7 + [F, P, SZ, P]),
         "clsa_decode_step_workspace_bytes": (SZ, [ctypes.POINTER(StepDesc)]),
         "clsa_decode_step": (I, [ctypes.POINTER(StepDesc), P, SZ, P]),
+        "clsa_decode_step_static": (I, [ctypes.POINTER(StepDesc), P]),
         "clsa_block_union_build": (I, [P] + [I] * 6 + [P, P, P, SZ, P]),
         "clsa_block_paged_attn": (I, [P, P, P, I, P, P, I, P, P] + [I] * 7 + [F, P]),
         "clsa_block_paged_attn_hm": (I, [P, P, P, I, P, P, I, P, P] + [I] * 7 + [F, P]),
@@ -320,6 +321,12 @@ class DecodeStep:
     def run(self) -> None:
         rc = self._fn(self._desc_ref, ctypes.c_void_p(self.ws.data_ptr()), self.ws.numel(), _stream())
         _check(rc, "clsa_decode_step")
+
+    def run_static(self) -> None:
+        """The same step through clsa_decode_step_static (the library's own
+        device scratch instead of self.ws; allocates nothing)."""
+        rc = load().clsa_decode_step_static(self._desc_ref, _stream())
+        _check(rc, "clsa_decode_step_static")
 
 
 def decode_step(layer_src, q, k_cache, v_cache, q_idx, k_idx, w, k, kv_len=None, scale=0.0):

@@ -20,7 +20,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libclsa.so")
 SOURCES = ["api.cpp", "index_score.hip", "topk.hip", "sparse_attn.hip", "block_union.hip",
-           "block_attn.hip", "cache_append.hip"]
+           "block_attn.hip", "cache_append.hip", "static_step.hip"]
 ARCH = "gfx950"
 
 
