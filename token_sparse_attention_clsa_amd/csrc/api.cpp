@@ -40,12 +40,14 @@ struct Carver {
 };
 
 struct TopkWs {
-  size_t counts, cand, spill, total;
+  size_t arrivals, arrival_words, counts, cand, spill, total;
 };
 TopkWs topk_ws(int rows, int kv_len) {
   const TopkBuffers tb = topk_buffers(rows, kv_len);
   Carver c;
   TopkWs w;
+  w.arrival_words = tb.arrival_words;
+  w.arrivals = c.add(tb.arrival_words * 4);
   w.counts = c.add(tb.counts_words * 4);
   w.cand = c.add(tb.cand_words * 4);
   w.spill = c.add(tb.spill_words * 4);
@@ -196,7 +198,7 @@ int clsa_index_score(const void* q_idx, const void* k_idx, int idx_dtype, const 
   int rc = check_index_args(q_idx, k_idx, idx_dtype, w, scores, B, T, H_I, D_I, kv_len, L_cap);
   if (rc) return rc;
   return launch_index_score(q_idx, k_idx, idx_dtype, w, scores, B, T, H_I, D_I, kv_len, L_cap,
-                            static_cast<hipStream_t>(stream));
+                            ZeroJob{}, static_cast<hipStream_t>(stream));
 }
 
 int clsa_topk_margin(const float* scores, int B, int T, int kv_len, int k,
@@ -213,10 +215,13 @@ int clsa_topk_margin(const float* scores, int B, int T, int kv_len, int k,
     return set_error(CLSA_ERR_WORKSPACE, "topk: workspace of %zu bytes (256-aligned) required, got %zu",
                      L.total, ws ? ws_bytes : (size_t)0);
   char* base = static_cast<char*>(ws);
+  uint32_t* arrivals = reinterpret_cast<uint32_t*>(base + L.arrivals);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (topk_uses_arrivals(B * T, kv_len, k) && (rc = zero_words(arrivals, L.arrival_words, s))) return rc;
   return launch_topk(scores, B, T, kv_len, k, k_per_query, margin, idx, kept,
                      reinterpret_cast<uint32_t*>(base + L.counts),
                      reinterpret_cast<int32_t*>(base + L.cand),
-                     reinterpret_cast<int32_t*>(base + L.spill), static_cast<hipStream_t>(stream));
+                     reinterpret_cast<int32_t*>(base + L.spill), arrivals, s);
 }
 
 int clsa_topk_vark(const float* scores, int B, int T, int kv_len, int k, const int32_t* k_per_query,
@@ -311,6 +316,7 @@ int clsa_decode_step(const clsa_step_desc* d, void* ws, size_t ws_bytes, void* s
                      ws ? ws_bytes : (size_t)0);
   hipStream_t s = static_cast<hipStream_t>(stream);
   char* base = static_cast<char*>(ws);
+  uint32_t* arrivals = reinterpret_cast<uint32_t*>(base + L.topk.arrivals);
   uint32_t* counts = reinterpret_cast<uint32_t*>(base + L.topk.counts);
   int32_t* cand = reinterpret_cast<int32_t*>(base + L.topk.cand);
   int32_t* spill = reinterpret_cast<int32_t*>(base + L.topk.spill);
@@ -323,15 +329,19 @@ int clsa_decode_step(const clsa_step_desc* d, void* ws, size_t ws_bytes, void* s
   int32_t* kept = d->k_per_query != nullptr || margin < INFINITY
                       ? reinterpret_cast<int32_t*>(base + L.kept)
                       : nullptr;
+  // The one-launch top-k needs its arrival words zero: each F layer's
+  // indexer kernel clears them before the top-k that follows it runs.
+  ZeroJob zj;
+  if (topk_uses_arrivals(d->B * d->T, d->kv_len, d->k)) zj = ZeroJob{arrivals, (int)L.topk.arrival_words};
   for (int l = 0; l < d->n_layers; l++) {
     if ((rc = record(d->events, 4 * l, s))) return rc;
     if (d->layer_src[l] == l) {
       rc = launch_index_score(d->q_idx[l], d->k_idx[l], d->idx_dtype, d->w[l], scores, d->B, d->T,
-                              d->H_I, d->D_I, d->kv_len, d->L_cap, s);
+                              d->H_I, d->D_I, d->kv_len, d->L_cap, zj, s);
       if (rc) return rc;
       if ((rc = record(d->events, 4 * l + 1, s))) return rc;
       rc = launch_topk(scores, d->B, d->T, d->kv_len, d->k, d->k_per_query, margin, d->idx_out,
-                       kept, counts, cand, spill, s);
+                       kept, counts, cand, spill, arrivals, s);
       if (rc) return rc;
     } else if ((rc = record(d->events, 4 * l + 1, s))) {
       return rc;

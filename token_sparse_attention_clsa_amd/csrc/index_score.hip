@@ -68,8 +68,12 @@ template <int DT, int DI, int HI>
 __global__ __launch_bounds__(kIdxThreads) void idx_score_mfma(
     const uint8_t* __restrict__ q_idx, const uint8_t* __restrict__ k_idx,
     const float* __restrict__ w, float* __restrict__ scores, int T, int kv_len, int L_cap,
-    int keys_per_wg) {
+    int keys_per_wg, uint32_t* __restrict__ zero_p, int zero_n) {
   using E = IdxElem<DT>;
+  // Words the step's next kernel needs zero (top-k arrival words): cleared
+  // here, so that kernel needs no launch of its own for it.
+  if (zero_n && blockIdx.x == 0 && blockIdx.y == 0)
+    for (int i = threadIdx.x; i < zero_n; i += kIdxThreads) zero_p[i] = 0u;
   constexpr int NS = DI / 32;          // k-steps per key row
   constexpr int NH = HI / 16;          // head tiles
   constexpr int SPAN = DI / 4 * E::bytes;  // bytes of a key row per lane
@@ -175,8 +179,10 @@ template <int DT, int DI, int HI>
 __global__ __launch_bounds__(kQB * kWave) void idx_score_multi(
     const uint8_t* __restrict__ q_idx, const uint8_t* __restrict__ k_idx,
     const float* __restrict__ w, float* __restrict__ scores, int T, int kv_len, int L_cap,
-    int keys_per_split) {
+    int keys_per_split, uint32_t* __restrict__ zero_p, int zero_n) {
   using E = IdxElem<DT>;
+  if (zero_n && blockIdx.x == 0 && blockIdx.y == 0)
+    for (int i = threadIdx.x; i < zero_n; i += kQB * kWave) zero_p[i] = 0u;
   constexpr int NS = DI / 32;
   constexpr int NH = HI / 16;
   constexpr int ROWB = DI * E::bytes;          // bytes of one key row: 64, 128 or 256
@@ -289,8 +295,11 @@ __global__ __launch_bounds__(kF32Threads) void idx_score_f32(const float* __rest
                                                      const float* __restrict__ k_idx,
                                                      const float* __restrict__ w,
                                                      float* __restrict__ scores, int T, int H,
-                                                     int D, int kv_len, int L_cap) {
+                                                     int D, int kv_len, int L_cap,
+                                                     uint32_t* __restrict__ zero_p, int zero_n) {
   extern __shared__ float sh[];
+  if (zero_n && blockIdx.x == 0 && blockIdx.y == 0)
+    for (int i = threadIdx.x; i < zero_n; i += kF32Threads) zero_p[i] = 0u;
   const int bt = blockIdx.y;
   const int b = bt / T, t = bt % T;
   const int vis = kv_len - T + t + 1;
@@ -316,7 +325,7 @@ __global__ __launch_bounds__(kF32Threads) void idx_score_f32(const float* __rest
 
 template <int DT, int DI, int HI>
 int launch_mfma(const void* q, const void* k, const float* w, float* scores, int B, int T,
-                int kv_len, int L_cap, hipStream_t stream) {
+                int kv_len, int L_cap, const ZeroJob& z, hipStream_t stream) {
   if (T >= kQB) {
     // Split the keys so that about 4096 workgroups run (16 per CU; at least 8
     // key tiles each). Measured on 2048 queries x 133120 keys: 3.09 ms against
@@ -333,7 +342,7 @@ int launch_mfma(const void* q, const void* k, const float* w, float* scores, int
     dim3 grid(splits, groups);
     hipLaunchKernelGGL((idx_score_multi<DT, DI, HI>), grid, dim3(kQB * kWave), 0, stream,
                        static_cast<const uint8_t*>(q), static_cast<const uint8_t*>(k), w, scores, T,
-                       kv_len, L_cap, keys);
+                       kv_len, L_cap, keys, z.p, z.n);
     return check_launch("idx_score_multi");
   }
   // About one workgroup per CU (256 in all) measured best at every decode
@@ -346,27 +355,27 @@ int launch_mfma(const void* q, const void* k, const float* w, float* scores, int
   dim3 grid((kv_len + keys_per_wg - 1) / keys_per_wg, B * T);
   hipLaunchKernelGGL((idx_score_mfma<DT, DI, HI>), grid, dim3(kIdxThreads), 0, stream,
                      static_cast<const uint8_t*>(q), static_cast<const uint8_t*>(k), w, scores, T,
-                     kv_len, L_cap, keys_per_wg);
+                     kv_len, L_cap, keys_per_wg, z.p, z.n);
   return check_launch("idx_score_mfma");
 }
 
 template <int DT, int DI>
 int dispatch_heads(int H_I, const void* q, const void* k, const float* w, float* scores, int B,
-                   int T, int kv_len, int L_cap, hipStream_t stream) {
+                   int T, int kv_len, int L_cap, const ZeroJob& z, hipStream_t stream) {
   switch (H_I) {
-    case 16: return launch_mfma<DT, DI, 16>(q, k, w, scores, B, T, kv_len, L_cap, stream);
-    case 32: return launch_mfma<DT, DI, 32>(q, k, w, scores, B, T, kv_len, L_cap, stream);
-    case 48: return launch_mfma<DT, DI, 48>(q, k, w, scores, B, T, kv_len, L_cap, stream);
-    case 64: return launch_mfma<DT, DI, 64>(q, k, w, scores, B, T, kv_len, L_cap, stream);
+    case 16: return launch_mfma<DT, DI, 16>(q, k, w, scores, B, T, kv_len, L_cap, z, stream);
+    case 32: return launch_mfma<DT, DI, 32>(q, k, w, scores, B, T, kv_len, L_cap, z, stream);
+    case 48: return launch_mfma<DT, DI, 48>(q, k, w, scores, B, T, kv_len, L_cap, z, stream);
+    case 64: return launch_mfma<DT, DI, 64>(q, k, w, scores, B, T, kv_len, L_cap, z, stream);
   }
   return set_error(CLSA_ERR_UNSUPPORTED, "index_score: H_I=%d", H_I);
 }
 
 template <int DT>
 int dispatch_dim(int H_I, int D_I, const void* q, const void* k, const float* w, float* scores,
-                 int B, int T, int kv_len, int L_cap, hipStream_t stream) {
-  if (D_I == 64) return dispatch_heads<DT, 64>(H_I, q, k, w, scores, B, T, kv_len, L_cap, stream);
-  if (D_I == 128) return dispatch_heads<DT, 128>(H_I, q, k, w, scores, B, T, kv_len, L_cap, stream);
+                 int B, int T, int kv_len, int L_cap, const ZeroJob& z, hipStream_t stream) {
+  if (D_I == 64) return dispatch_heads<DT, 64>(H_I, q, k, w, scores, B, T, kv_len, L_cap, z, stream);
+  if (D_I == 128) return dispatch_heads<DT, 128>(H_I, q, k, w, scores, B, T, kv_len, L_cap, z, stream);
   return set_error(CLSA_ERR_UNSUPPORTED, "index_score: D_I=%d", D_I);
 }
 
@@ -381,18 +390,18 @@ bool index_score_supported(int idx_dtype, int H_I, int D_I) {
 
 int launch_index_score(const void* q_idx, const void* k_idx, int idx_dtype, const float* w,
                        float* scores, int B, int T, int H_I, int D_I, int kv_len, int L_cap,
-                       hipStream_t stream) {
+                       const ZeroJob& z, hipStream_t stream) {
   if (idx_dtype == CLSA_F32) {
     dim3 grid((kv_len + kF32Threads - 1) / kF32Threads, B * T);
     size_t lds = sizeof(float) * ((size_t)H_I * D_I + H_I);
     hipLaunchKernelGGL(idx_score_f32, grid, dim3(kF32Threads), lds, stream,
                        static_cast<const float*>(q_idx), static_cast<const float*>(k_idx), w,
-                       scores, T, H_I, D_I, kv_len, L_cap);
+                       scores, T, H_I, D_I, kv_len, L_cap, z.p, z.n);
     return check_launch("idx_score_f32");
   }
   if (idx_dtype == CLSA_BF16)
-    return dispatch_dim<CLSA_BF16>(H_I, D_I, q_idx, k_idx, w, scores, B, T, kv_len, L_cap, stream);
-  return dispatch_dim<CLSA_FP8_E4M3FN>(H_I, D_I, q_idx, k_idx, w, scores, B, T, kv_len, L_cap,
+    return dispatch_dim<CLSA_BF16>(H_I, D_I, q_idx, k_idx, w, scores, B, T, kv_len, L_cap, z, stream);
+  return dispatch_dim<CLSA_FP8_E4M3FN>(H_I, D_I, q_idx, k_idx, w, scores, B, T, kv_len, L_cap, z,
                                        stream);
 }
 

@@ -19,9 +19,14 @@ int launch_cache_append(const AppendJob* jobs, int n_jobs, int B, int T, int pos
                         hipStream_t stream);
 
 // ---- indexer score ---------------------------------------------------------
+// Words a launch clears besides its own work (n = 0: none).
+struct ZeroJob {
+  uint32_t* p = nullptr;
+  int n = 0;
+};
 int launch_index_score(const void* q_idx, const void* k_idx, int idx_dtype, const float* w,
                        float* scores, int B, int T, int H_I, int D_I, int kv_len, int L_cap,
-                       hipStream_t stream);
+                       const ZeroJob& z, hipStream_t stream);
 bool index_score_supported(int idx_dtype, int H_I, int D_I);
 
 // ---- top-k -----------------------------------------------------------------
@@ -33,17 +38,20 @@ constexpr int kTopkChunk = 4096;
 constexpr int kTopkSegCap = 1024;     // candidates kept per chunk
 constexpr int kTopkMaxChunks = 1024;  // kv_len <= 4M
 struct TopkBuffers {
-  int nchunks;
-  size_t counts_words, cand_words, spill_words;
+  int nchunks, cstride;  // chunks per row; counts words per row
+  size_t counts_words, cand_words, spill_words, arrival_words;
 };
 TopkBuffers topk_buffers(int rows, int kv_len);
+// Whether launch_topk takes the one-launch path, whose arrival words
+// (arrival_words u32) must be zero before the launch (it leaves them zero).
+bool topk_uses_arrivals(int rows, int kv_len, int k);
 // k_rows: NULL, or a device int32 [B*T] of per-row counts (clamped to [0, k]).
 // margin: +inf, or the ordered-skipping margin (>= 0): each row keeps only the
 // selected positions scoring at least (row maximum - margin). kept: NULL, or
 // a device int32 [B*T] receiving each row's count of kept positions.
 int launch_topk(const float* scores, int B, int T, int kv_len, int k, const int32_t* k_rows,
                 float margin, int32_t* idx, int32_t* kept, uint32_t* counts, int32_t* cand,
-                int32_t* spill, hipStream_t stream);
+                int32_t* spill, uint32_t* arrivals, hipStream_t stream);
 
 // ---- sparse attention --------------------------------------------------------
 // Buffer: partials [attn_partial_floats(...)] f32 (split states; unused when

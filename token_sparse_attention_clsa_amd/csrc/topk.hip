@@ -40,6 +40,8 @@
 // theta, theta becomes key(thr) and every key equal to it is taken; the rest
 // of the row is -1.
 #include <climits>
+#include <mutex>
+#include <stdlib.h>
 
 #include "kernels.h"
 
@@ -57,6 +59,8 @@ constexpr int kTile = 16384;       // fallback tile: 16 waves x 1024 consecutive
 constexpr int kLdsCap = 12288;     // candidates kept in LDS
 constexpr int kHistCopies = 2;     // fallback histogram copies
 constexpr int kLdsRow = 16384;     // rows up to this length: one launch, row in LDS
+constexpr int kFusedMaxRows = 64;    // topk_fused: at most this many rows ...
+constexpr int kFusedMaxChunks = 64;  // ... of at most this many 4096-element chunks
 
 // Finds the bin b (scanning bins from high to low) where the running count
 // first reaches `need`; res[0] = b, res[1] = count in bins above b. Thread t
@@ -431,7 +435,7 @@ __global__ __launch_bounds__(kFilterThreads) void topk_filter(const float* __res
                                                               int2* __restrict__ cand, int T,
                                                               int kv_len, int k,
                                                               const int32_t* __restrict__ k_rows,
-                                                              int nchunks, int cpw) {
+                                                              int nchunks, int cstride, int cpw) {
   __shared__ __attribute__((aligned(16))) uint32_t h[kBins0];
   __shared__ int tmp[17];
   __shared__ int res[3];
@@ -439,7 +443,7 @@ __global__ __launch_bounds__(kFilterThreads) void topk_filter(const float* __res
   const int row = blockIdx.y;
   const int vis = kv_len - T + (row % T) + 1;
   const int ci0 = blockIdx.x * cpw, ci1 = min(nchunks, ci0 + cpw);
-  uint32_t* cnt = counts + (size_t)row * nchunks;
+  uint32_t* cnt = counts + (size_t)row * cstride;
   if (k_rows) k = min(max(k_rows[row], 0), k);
   if (vis <= k || ci0 * kChunk >= vis || k == 0) {
     for (int ci = ci0 + threadIdx.x; ci < ci1; ci += kFilterThreads) cnt[ci] = 0u;
@@ -579,25 +583,34 @@ __device__ bool row_prologue(const float* srow, int vis, int& k, const int32_t* 
   return true;
 }
 
-// grid (rows), block 1024.
-__global__ __launch_bounds__(kThreads) void topk_select(const float* __restrict__ scores,
-                                                        const uint32_t* __restrict__ counts,
-                                                        const int2* __restrict__ cand,
-                                                        int32_t* __restrict__ spill,
-                                                        int32_t* __restrict__ idx, int T,
-                                                        int kv_len, int k,
-                                                        const int32_t* __restrict__ k_rows,
-                                                        int nchunks, float margin,
-                                                        int32_t* __restrict__ kept) {
-  __shared__ __attribute__((aligned(16))) uint32_t h[kBins0 * (1 + kHistCopies)];
-  __shared__ int32_t lpos[kLdsCap];
-  __shared__ uint32_t lkey[kLdsCap];
-  __shared__ int off[kTopkMaxChunks + 1];
-  __shared__ uint32_t mm[2][kWaves];
-  __shared__ int wtot[kWaves + 1];
-  __shared__ int tmp[17];
-  __shared__ int res[3];
-  const int row = blockIdx.x;
+// LDS of the selection (one 1024-thread workgroup per row).
+struct SelectLds {
+  uint32_t h[kBins0 * (1 + kHistCopies)];
+  int32_t lpos[kLdsCap];
+  uint32_t lkey[kLdsCap];
+  int off[kTopkMaxChunks + 1];
+  uint32_t mm[2][kWaves];
+  int wtot[kWaves + 1];
+  int tmp[17];
+  int res[3];
+};
+
+// Selection of row `row` from the filter's candidate segments (counts at
+// counts[row * cstride + c]); every thread of the 1024-thread workgroup
+// calls it. trust_segments false: redo the row from its scores alone.
+__device__ __forceinline__ void select_row(int row, const float* __restrict__ scores, const uint32_t* __restrict__ counts,
+                           int cstride, const int2* __restrict__ cand, int32_t* __restrict__ spill,
+                           int32_t* __restrict__ idx, int T, int kv_len, int k,
+                           const int32_t* __restrict__ k_rows, int nchunks, float margin,
+                           int32_t* __restrict__ kept, bool trust_segments, SelectLds& L) {
+  uint32_t* h = L.h;
+  int32_t* lpos = L.lpos;
+  uint32_t* lkey = L.lkey;
+  int* off = L.off;
+  uint32_t (*mm)[kWaves] = L.mm;
+  int* wtot = L.wtot;
+  int* tmp = L.tmp;
+  int* res = L.res;
   const int vis = kv_len - T + (row % T) + 1;
   int32_t* out = idx + (size_t)row * k;  // k slots
   int32_t* kept_row = kept ? kept + row : nullptr;
@@ -624,13 +637,13 @@ __global__ __launch_bounds__(kThreads) void topk_select(const float* __restrict_
   bool overflow;
   {
     const int c = threadIdx.x;
-    const int v = c < nchunks ? (int)counts[(size_t)row * nchunks + c] : 0;
+    const int v = c < nchunks ? (int)counts[(size_t)row * cstride + c] : 0;
     const int o = block_exclusive_scan<kThreads>(v, tmp, &n);
     if (c < nchunks) off[c] = o;
     if (c == 0) off[nchunks] = n;
     overflow = __syncthreads_or(v > kTopkSegCap) != 0;
   }
-  if (n >= k && !overflow) {
+  if (n >= k && !overflow && trust_segments) {
     uint32_t mn = 0xffffffffu, mx = 0u;  // key range of the candidates
     if (n <= kLdsCap) {
       if (gc < nchunks) {
@@ -688,6 +701,172 @@ __global__ __launch_bounds__(kThreads) void topk_select(const float* __restrict_
   select_and_emit(acc, n, k - above, b0 << 20, 1ull << 20, h, res, tmp, out, k, mkey, kept_row);
 }
 
+// grid (rows), block 1024.
+__global__ __launch_bounds__(kThreads) void topk_select(const float* __restrict__ scores,
+                                                        const uint32_t* __restrict__ counts,
+                                                        const int2* __restrict__ cand,
+                                                        int32_t* __restrict__ spill,
+                                                        int32_t* __restrict__ idx, int T,
+                                                        int kv_len, int k,
+                                                        const int32_t* __restrict__ k_rows,
+                                                        int nchunks, int cstride, float margin,
+                                                        int32_t* __restrict__ kept) {
+  __shared__ __attribute__((aligned(16))) SelectLds L;
+  select_row(blockIdx.x, scores, counts, cstride, cand, spill, idx, T, kv_len, k, k_rows, nchunks, margin,
+             kept, true, L);
+}
+
+
+// ---------------------------------------------------------------------------
+// One-launch form for few rows (decode): grid = rows x filter workgroups,
+// 1024 threads each. A workgroup takes cpw consecutive 4096-element chunks
+// of its row, computes the row's sample threshold as topk_filter does and
+// writes the chunks' candidate segments and counts; it then waits until its
+// stores are done and counts itself in the row's arrival word. The
+// workgroup that arrives last selects the row (topk_select's work) from the
+// segments. Segments and counts are plain stores into the L2 of the
+// writer's XCD; the selecting workgroup reads them through its own L2, so
+// all of a row's workgroups must run on one XCD. The grid is laid out for
+// that (workgroups go to the XCDs in turn, XCD = workgroup id mod n_xcd, and
+// row r's workgroups all get ids = r mod n_xcd), and the arrival word checks
+// it: each arrival adds 1, its XCD number x (register XCC_ID) and x^2 to
+// three fields; the sums equal (n x, n x^2) only when all n arrivals ran on
+// XCD x. Otherwise the last arrival redoes the row from its scores alone
+// (the select's full-row path), which reads nothing the filter wrote.
+// Arrival words: one 64-bit word per row, 128 bytes apart (count bits 0..15,
+// sum of x bits 16..31, sum of x^2 bits 32..63), zero before the launch and
+// reset to zero by the row's last arrival.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t xcc_id() {
+  return __builtin_amdgcn_s_getreg((3 << 11) | 20);  // HW_REG_XCC_ID, bits [3:0]
+}
+
+constexpr int kFusedPer = kChunk / kThreads;  // elements of a chunk per thread (4)
+
+__global__ __launch_bounds__(kThreads) void topk_fused(const float* __restrict__ scores,
+                                                       uint32_t* __restrict__ counts, int2* __restrict__ cand,
+                                                       int32_t* __restrict__ spill, int32_t* __restrict__ idx,
+                                                       int T, int kv_len, int k,
+                                                       const int32_t* __restrict__ k_rows, int nchunks,
+                                                       int cstride, int cpw, int wpr, int rows, int n_xcd,
+                                                       float margin, int32_t* __restrict__ kept,
+                                                       uint64_t* __restrict__ arrivals, int force_redo) {
+  __shared__ __attribute__((aligned(16))) SelectLds L;
+  __shared__ int s_flag;
+  const int x = blockIdx.x % n_xcd, slot = blockIdx.x / n_xcd;
+  const int row = x + n_xcd * (slot / wpr);
+  if (row >= rows) return;  // no row for this workgroup (uniform)
+  const int ci0 = (slot % wpr) * cpw, ci1 = min(nchunks, ci0 + cpw);
+  const int vis = kv_len - T + (row % T) + 1;
+  const float* srow = scores + (size_t)row * kv_len;
+  uint32_t* cnt = counts + (size_t)row * cstride;
+  int kr = k_rows ? min(max(k_rows[row], 0), k) : k;
+  uint32_t* h = L.h;
+  int* tmp = L.tmp;
+  int* res = L.res;
+  if (vis <= kr || ci0 * kChunk >= vis || kr == 0) {
+    for (int ci = ci0 + threadIdx.x; ci < ci1; ci += kThreads) cnt[ci] = 0u;
+  } else {
+    // This thread's 4 consecutive elements of the first chunk, then the
+    // row's sample (2 elements per thread), both in flight together.
+    const bool a16 = (reinterpret_cast<uintptr_t>(srow) & 15) == 0;
+    float xs[kFusedPer];
+    if (a16)
+      load4<true>(srow, ci0 * kChunk + threadIdx.x * kFusedPer, vis, xs);
+    else
+      load4<false>(srow, ci0 * kChunk + threadIdx.x * kFusedPer, vis, xs);
+    const int m = min(kSample, vis);
+    constexpr int kRuns = kSample / kSampleRun;
+    constexpr int kPer = kSample / kThreads;
+    float sv[kPer];
+#pragma unroll
+    for (int j = 0; j < kPer; j++) {
+      const int i = threadIdx.x + j * kThreads;
+      const int pos = vis <= kSample
+                          ? i
+                          : (int)((long)(i / kSampleRun) * (vis - kSampleRun) / (kRuns - 1)) + i % kSampleRun;
+      sv[j] = i < m ? srow[pos] : 0.f;
+    }
+    uint32_t sk[kPer];
+    uint32_t mn = 0xffffffffu, mx = 0u;
+#pragma unroll
+    for (int j = 0; j < kPer; j++) {
+      sk[j] = score_key(sv[j]);
+      if (threadIdx.x + j * kThreads < m) {
+        mn = min(mn, sk[j]);
+        mx = max(mx, sk[j]);
+      }
+    }
+    for (int i = threadIdx.x; i < kBins0; i += kThreads) h[i] = 0u;
+    block_minmax(mn, mx, L.mm);  // its barrier also orders the clear before the counts
+    const uint64_t span = (uint64_t)(mx - mn) + 1;
+    const int bits = span == 1 ? 0 : 64 - __clzll(span - 1);
+    const int sh = bits > 12 ? bits - 12 : 0;
+    const int nb = 1 << (bits - sh);
+#pragma unroll
+    for (int j = 0; j < kPer; j++)
+      if (threadIdx.x + j * kThreads < m) atomicAdd(&h[(sk[j] - mn) >> sh], 1u);
+    __syncthreads();
+    const long expect = ((long)kr * m + vis - 1) / vis;  // rank of the k-th key in the sample
+    find_bin<kThreads>(h, nb, (int)min((long)m, 2 * expect + 8), res, tmp);
+    const uint32_t thr = mn + ((uint32_t)res[0] << sh);
+    for (int ci = ci0; ci < ci1; ci++) {  // uniform over the workgroup
+      const int c0 = ci * kChunk;
+      if (c0 >= vis) {
+        if (threadIdx.x == 0) cnt[ci] = 0u;
+        continue;
+      }
+      const int e = c0 + threadIdx.x * kFusedPer;
+      if (ci != ci0) {
+        if (a16)
+          load4<true>(srow, e, vis, xs);
+        else
+          load4<false>(srow, e, vis, xs);
+      }
+      uint32_t key[kFusedPer];
+      uint32_t flags = 0;
+      int c = 0;
+#pragma unroll
+      for (int j = 0; j < kFusedPer; j++) {
+        key[j] = score_key(xs[j]);
+        if (e + j < vis && key[j] >= thr) {
+          flags |= 1u << j;
+          c++;
+        }
+      }
+      int total;
+      int o = block_exclusive_scan<kThreads>(c, tmp, &total);
+      int2* seg = cand + ((size_t)row * nchunks + ci) * kTopkSegCap;
+#pragma unroll
+      for (int j = 0; j < kFusedPer; j++)
+        if (flags >> j & 1u) {
+          if (o < kTopkSegCap) seg[o] = make_int2(e + j, (int)key[j]);
+          o++;
+        }
+      if (threadIdx.x == 0) cnt[ci] = (uint32_t)total;  // above kTopkSegCap: the row is redone
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0);  // this thread's segment and count stores are done (in this XCD's L2)
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint64_t xi = xcc_id() & 15u;
+    const uint64_t mine = 1ull | (xi << 16) | ((xi * xi) << 32);
+    uint64_t* word = arrivals + (size_t)row * 16;
+    const uint64_t now = __hip_atomic_fetch_add(word, mine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + mine;
+    int flag = 0;
+    if ((now & 0xffffu) == (uint64_t)wpr) {  // every workgroup of the row has arrived
+      __hip_atomic_exchange(word, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const bool one_xcd =
+          ((now >> 16) & 0xffffu) == (uint64_t)wpr * xi && (now >> 32) == (uint64_t)wpr * xi * xi;
+      flag = one_xcd && !force_redo ? 1 : 2;
+    }
+    s_flag = flag;
+  }
+  __syncthreads();
+  if (s_flag == 0) return;
+  select_row(row, scores, counts, cstride, cand, spill, idx, T, kv_len, k, k_rows, nchunks, margin, kept,
+             s_flag == 1, L);
+}
 
 // A whole row held in LDS as keys.
 struct RowCand {
@@ -796,15 +975,50 @@ int zero_words(uint32_t* p, size_t n, hipStream_t stream) {
 TopkBuffers topk_buffers(int rows, int kv_len) {
   TopkBuffers b;
   b.nchunks = (kv_len + kChunk - 1) / kChunk;
-  b.counts_words = (size_t)rows * b.nchunks;
+  b.cstride = (b.nchunks + 31) / 32 * 32;  // a row's counts start on their own 128-byte line
+  b.counts_words = (size_t)rows * b.cstride;
   b.cand_words = (size_t)rows * b.nchunks * kTopkSegCap * 2;
   b.spill_words = (size_t)rows * kv_len;
+  b.arrival_words = (size_t)rows * 32;  // one 64-bit word per row, 128 bytes apart
   return b;
 }
 
+bool topk_uses_arrivals(int rows, int kv_len, int k) {
+  const int nchunks = (kv_len + kChunk - 1) / kChunk;
+  const bool lds = kv_len <= kLdsRow / 2 || (kv_len <= kLdsRow && 8L * k >= kv_len);
+  return !lds && rows <= kFusedMaxRows && nchunks <= kFusedMaxChunks;
+}
+
+namespace {
+// XCDs of the current device (gfx950: 32 CUs each); workgroup i runs on XCD
+// i % n_xcd. Used for placement only: topk_fused checks where it ran.
+int device_xcds() {
+  static std::mutex mu;
+  static int cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 1;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!cached[dev]) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) cus = 0;
+    cached[dev] = (cus >= 32 && cus % 32 == 0) ? std::min(cus / 32, 16) : 1;
+  }
+  return cached[dev];
+}
+// CLSA_TOPK_FORCE_REDO=1: the one-launch top-k redoes every row from its
+// scores (tests of that path).
+int force_redo() {
+  static const int v = [] {
+    const char* e = getenv("CLSA_TOPK_FORCE_REDO");
+    return e && e[0] == '1' ? 1 : 0;
+  }();
+  return v;
+}
+}  // namespace
+
 int launch_topk(const float* scores, int B, int T, int kv_len, int k, const int32_t* k_rows,
                 float margin, int32_t* idx, int32_t* kept, uint32_t* counts, int32_t* cand,
-                int32_t* spill, hipStream_t stream) {
+                int32_t* spill, uint32_t* arrivals, hipStream_t stream) {
   const int rows = B * T;
   const TopkBuffers tb = topk_buffers(rows, kv_len);
   if (tb.nchunks > kTopkMaxChunks)
@@ -822,17 +1036,27 @@ int launch_topk(const float* scores, int B, int T, int kv_len, int k, const int3
     return check_launch("topk_lds");
   }
   int2* segs = reinterpret_cast<int2*>(cand);
+  if (topk_uses_arrivals(rows, kv_len, k)) {
+    // Few rows: one launch, the selection done by each row's last workgroup.
+    const int n_xcd = device_xcds();
+    const int wpr = tb.nchunks;  // one 4096-element chunk per workgroup
+    const int rpx = (rows + n_xcd - 1) / n_xcd;
+    hipLaunchKernelGGL(topk_fused, dim3((unsigned)(n_xcd * rpx * wpr)), dim3(kThreads), 0, stream, scores,
+                       counts, segs, spill, idx, T, kv_len, k, k_rows, tb.nchunks, tb.cstride, 1, wpr,
+                       rows, n_xcd, margin, kept, reinterpret_cast<uint64_t*>(arrivals), force_redo());
+    return check_launch("topk_fused");
+  }
   // Chunks per filter workgroup: one while the grid stays small (decode),
   // more when rows are many (a chunk's queries), so the row's threshold is
   // computed once per cpw chunks; about 8192 workgroups at most.
   const long total_chunks = (long)rows * tb.nchunks;
   int cpw = (int)min((long)tb.nchunks, max(1L, total_chunks / 8192));
   hipLaunchKernelGGL(topk_filter, dim3((tb.nchunks + cpw - 1) / cpw, rows), dim3(kFilterThreads), 0,
-                     stream, scores, counts, segs, T, kv_len, k, k_rows, tb.nchunks, cpw);
+                     stream, scores, counts, segs, T, kv_len, k, k_rows, tb.nchunks, tb.cstride, cpw);
   int rc = check_launch("topk_filter");
   if (rc) return rc;
   hipLaunchKernelGGL(topk_select, dim3(rows), dim3(kThreads), 0, stream, scores, counts, segs, spill,
-                     idx, T, kv_len, k, k_rows, tb.nchunks, margin, kept);
+                     idx, T, kv_len, k, k_rows, tb.nchunks, tb.cstride, margin, kept);
   return check_launch("topk_select");
 }
 
