@@ -185,8 +185,9 @@ int clsa_topk_margin(const float* scores, int B, int T, int kv_len, int k,
  *   out     [B, T, Hq, D]         dtype output (BF16 rounded once, to nearest even)
  *   lse     [B, T, Hq]            float32 output, or NULL
  * scale <= 0 selects 1/sqrt(D). Softmax and accumulation are float32; with
- * BF16 the probabilities enter the matrix-core P.V product rounded to bf16
- * (the normaliser stays float32), F32 keeps them in float32.
+ * BF16 the probabilities enter the matrix-core P.V product as a bf16 pair
+ * (hi = bf16(p), lo = bf16(p - hi): about 16 significant bits), F32 keeps
+ * them in float32.
  * Supported: D = 128, Hq / Hkv in {1, 2, 4, 8}.
  * Workspace: clsa_workspace_bytes(CLSA_OP_SPARSE_ATTN, B, T, Hq, Hkv, D, 0, k, 0).
  */

@@ -281,8 +281,9 @@ __global__ __launch_bounds__(kWave * kMaxWaves) void attn_split_kernel(
 //  - Softmax: one running max per head shared by the four lane groups (a
 //    cross-group max through v_permlane16/32_swap), so the per-group partial
 //    sums add without rescaling; each exp is taken once.
-//  - Output: O^T[d, h] += V^T[d, key] . P^T[key, h], P rounded to bf16. The
-//    lane's 8 probabilities are already the B operand (k slot x = 4 * tile +
+//  - Output: O^T[d, h] += V^T[d, key] . P^T[key, h], P split into bf16 hi
+//    and bf16 lo parts (two products). The lane's 8 probabilities are
+//    already the B operand (k slot x = 4 * tile +
 //    r of lane group grp is key 16 * tile + 4 * grp + r). V^T goes through a
 //    per-wave LDS tile: each lane gathers 16-byte V row pieces (same keys as
 //    its probabilities, d = 8 * col + 0..7) and writes them transposed; the
@@ -441,9 +442,20 @@ __device__ __forceinline__ void kv_consume(const KvStep& f, MfmaState& st, const
 #pragma unroll
     for (int j = 0; j < 8; j++) st.o[j] *= alpha;
   }
+  // P enters the matrix cores as bf16 hi + bf16 lo: hi = bf16(p), lo =
+  // bf16(p - hi) (p - hi is exact in float32), so P carries about 16
+  // significant bits instead of 8; two products accumulate into O.
   const uint4 pb = make_uint4(pack_bf16(pr[0][0], pr[0][1]), pack_bf16(pr[0][2], pr[0][3]),
                               pack_bf16(pr[1][0], pr[1][1]), pack_bf16(pr[1][2], pr[1][3]));
+  const uint32_t pw[4] = {pb.x, pb.y, pb.z, pb.w};
+  uint32_t lw[4];
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    const float* pi = &pr[i / 2][2 * (i % 2)];
+    lw[i] = pack_bf16(pi[0] - __uint_as_float(pw[i] << 16), pi[1] - __uint_as_float(pw[i] & 0xffff0000u));
+  }
   const bf16x8 pf = __builtin_bit_cast(bf16x8, pb);
+  const bf16x8 pl = __builtin_bit_cast(bf16x8, make_uint4(lw[0], lw[1], lw[2], lw[3]));
   // The tile is private to the wave; the fences keep the compiler from
   // moving its accesses across the write/read phases.
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -459,6 +471,7 @@ __device__ __forceinline__ void kv_consume(const KvStep& f, MfmaState& st, const
   for (int j = 0; j < 8; j++) {
     const bf16x8 af = __builtin_bit_cast(bf16x8, make_uint4(lo[j].x, lo[j].y, hi[j].x, hi[j].y));
     st.o[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, pf, st.o[j], 0, 0, 0);
+    st.o[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, pl, st.o[j], 0, 0, 0);
   }
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
