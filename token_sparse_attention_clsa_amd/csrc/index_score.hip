@@ -63,6 +63,23 @@ struct IdxElem<CLSA_FP8_E4M3FN> {
   }
 };
 
+// With D_I = 128 the four 32-deep fp8 k-steps of a lane are one contiguous
+// 32-byte run of the row (lane group g holds d = 32 g .. 32 g + 31), which
+// is exactly the operand of gfx950's 128-deep fp8 MFMA: one
+// v_mfma_scale_f32_16x16x128_f8f6f4 (A and B in E4M3, scale exponents 127,
+// i.e. 1.0) replaces four v_mfma_f32_16x16x32_fp8_fp8. Measured on MI355X:
+// the 32-deep fp8 instruction runs at about the bf16 rate (1.9 PFLOP/s), the
+// 128-deep one at 4.8 PFLOP/s with the epilogue's VALU mostly hidden.
+typedef __attribute__((ext_vector_type(8))) int i32x8;
+__device__ __forceinline__ i32x8 cat4(long a, long b, long c, long d) {
+  return i32x8{(int)a, (int)(a >> 32), (int)b, (int)(b >> 32), (int)c, (int)(c >> 32), (int)d, (int)(d >> 32)};
+}
+__device__ __forceinline__ f32x4 mfma_fp8_k128(const i32x8& a, const i32x8& b, f32x4 c) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+template <int DT, int DI>
+constexpr bool kUseK128 = DT == CLSA_FP8_E4M3FN && DI == 128;
+
 // grid: (ceil(kv_len / keys_per_wg), B*T), block: 256.
 template <int DT, int DI, int HI>
 __global__ __launch_bounds__(kIdxThreads) void idx_score_mfma(
@@ -128,10 +145,17 @@ __global__ __launch_bounds__(kIdxThreads) void idx_score_mfma(
       f32x4 acc[NH];
 #pragma unroll
       for (int ht = 0; ht < NH; ht++) acc[ht] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if constexpr (kUseK128<DT, DI>) {
+        const i32x8 b8 = cat4(bf[j][0], bf[j][1], bf[j][2], bf[j][3]);
 #pragma unroll
-      for (int s = 0; s < NS; s++)
+        for (int ht = 0; ht < NH; ht++)
+          acc[ht] = mfma_fp8_k128(cat4(a[ht][0], a[ht][1], a[ht][2], a[ht][3]), b8, acc[ht]);
+      } else {
 #pragma unroll
-        for (int ht = 0; ht < NH; ht++) acc[ht] = E::mfma(a[ht][s], bf[j][s], acc[ht]);
+        for (int s = 0; s < NS; s++)
+#pragma unroll
+          for (int ht = 0; ht < NH; ht++) acc[ht] = E::mfma(a[ht][s], bf[j][s], acc[ht]);
+      }
       float v = 0.f;
 #pragma unroll
       for (int ht = 0; ht < NH; ht++)
@@ -159,7 +183,10 @@ __global__ __launch_bounds__(kIdxThreads) void idx_score_mfma(
 // so the per-tile wait for the transfer rarely waits on a store.
 // grid (key_splits, B * ceil(T / kQB)), block kQB * 64.
 constexpr int kQB = 8;
-constexpr int kKT = 64;
+// Keys per LDS tile: 16 KiB tiles, 64 keys of 256-byte rows (bf16 x 128) or
+// 128 keys of rows up to 128 bytes (fp8, or D_I = 64): each tile waits once
+// for its transfer and once at a barrier, so shorter rows take longer tiles.
+__host__ __device__ constexpr int key_tile(int rowb) { return rowb <= 128 ? 128 : 64; }
 typedef __attribute__((address_space(3))) void lds_void;
 
 // Lane group g (lanes 16 g .. 16 g + 15) receives v_g summed over the four
@@ -188,6 +215,8 @@ __global__ __launch_bounds__(kQB * kWave) void idx_score_multi(
   constexpr int ROWB = DI * E::bytes;          // bytes of one key row: 64, 128 or 256
   constexpr int CHUNKS = ROWB / 16;            // 16-byte chunks per row
   constexpr int RPS = 256 / ROWB;              // rows per 256-byte span
+  constexpr int kKT = key_tile(ROWB);          // keys per tile
+  constexpr int NR = kKT / 64;                 // results per lane per tile
   constexpr int NI = kKT * ROWB / 1024;        // 1 KiB transfers per tile
   static_assert(ROWB >= 64 && ROWB <= 256 && NI >= 1, "row size");
   __shared__ __attribute__((aligned(16))) uint8_t tile0[kKT * ROWB];
@@ -217,6 +246,10 @@ __global__ __launch_bounds__(kQB * kWave) void idx_score_multi(
   for (int ht = 0; ht < NH; ht++)
 #pragma unroll
     for (int r = 0; r < 4; r++) wv[ht][r] = w[(size_t)bt * HI + ht * 16 + 4 * grp + r];
+  i32x8 a8[kUseK128<DT, DI> ? NH : 1];  // the 128-deep fp8 operands (the same bytes as a)
+  if constexpr (kUseK128<DT, DI>)
+#pragma unroll
+    for (int ht = 0; ht < NH; ht++) a8[ht] = cat4(a[ht][0], a[ht][1], a[ht][2], a[ht][3]);
 
   const uint8_t* kbase = k_idx + (size_t)b * L_cap * ROWB;
   float* srow = scores + (size_t)bt * kv_len;
@@ -252,36 +285,55 @@ __global__ __launch_bounds__(kQB * kWave) void idx_score_multi(
     __builtin_amdgcn_s_waitcnt(0x0070); /* vmcnt(0) lgkmcnt(0) */                                    \
     asm volatile("s_barrier" ::: "memory");                                                           \
     if ((base) + kKT < kend) { CLSA_ISSUE((base) + kKT, NXT) }                                        \
-    if (active && prev_key < k1) srow[prev_key] = prev_key < vis ? prev_res : -INFINITY;              \
+    _Pragma("unroll") for (int r = 0; r < NR; r++)                                                    \
+      if (active && prev_key[r] < k1) srow[prev_key[r]] = prev_key[r] < vis ? prev_res[r] : -INFINITY; \
     float vs[kKT / 16];                                                                               \
     _Pragma("unroll") for (int j = 0; j < kKT / 16; j++) {                                            \
       f32x4 acc[NH];                                                                                  \
       _Pragma("unroll") for (int ht = 0; ht < NH; ht++) acc[ht] = f32x4{0.f, 0.f, 0.f, 0.f};          \
       const int r = j * 16 + col;                                                                     \
-      _Pragma("unroll") for (int s = 0; s < NS; s++) {                                                \
-        const int off = grp * (ROWB / 4) + 8 * s * E::bytes;                                          \
-        const typename E::frag bf = E::load((CUR) + CLSA_CHUNK_AT(r, off / 16) + off % 16);           \
-        _Pragma("unroll") for (int ht = 0; ht < NH; ht++) acc[ht] = E::mfma(a[ht][s], bf, acc[ht]);   \
+      if constexpr (kUseK128<DT, DI>) {                                                               \
+        typename E::frag bf[NS];                                                                      \
+        _Pragma("unroll") for (int s = 0; s < NS; s++) {                                              \
+          const int off = grp * (ROWB / 4) + 8 * s * E::bytes;                                        \
+          bf[s] = E::load((CUR) + CLSA_CHUNK_AT(r, off / 16) + off % 16);                             \
+        }                                                                                             \
+        const i32x8 b8 = cat4(bf[0], bf[1], bf[2], bf[3]);                                            \
+        _Pragma("unroll") for (int ht = 0; ht < NH; ht++) acc[ht] = mfma_fp8_k128(a8[ht], b8, acc[ht]); \
+      } else {                                                                                        \
+        _Pragma("unroll") for (int s = 0; s < NS; s++) {                                              \
+          const int off = grp * (ROWB / 4) + 8 * s * E::bytes;                                        \
+          const typename E::frag bf = E::load((CUR) + CLSA_CHUNK_AT(r, off / 16) + off % 16);         \
+          _Pragma("unroll") for (int ht = 0; ht < NH; ht++) acc[ht] = E::mfma(a[ht][s], bf, acc[ht]); \
+        }                                                                                             \
       }                                                                                               \
       float v = 0.f;                                                                                  \
       _Pragma("unroll") for (int ht = 0; ht < NH; ht++)                                               \
         _Pragma("unroll") for (int q = 0; q < 4; q++) v += wv[ht][q] * relu(acc[ht][q]);              \
       vs[j] = v;                                                                                      \
     }                                                                                                 \
-    const float res = group4_transpose_sum(vs[0], vs[1], vs[2], vs[3]);                               \
-    prev_key = (base) + grp * 16 + col;                                                               \
-    prev_res = res;                                                                                   \
+    _Pragma("unroll") for (int r = 0; r < NR; r++) {                                                  \
+      prev_res[r] = group4_transpose_sum(vs[4 * r], vs[4 * r + 1], vs[4 * r + 2], vs[4 * r + 3]);     \
+      prev_key[r] = (base) + 64 * r + grp * 16 + col;                                                 \
+    }                                                                                                 \
   }
 
-  int prev_key = k1;  // nothing to store before the first tile
-  float prev_res = 0.f;
+  int prev_key[NR];  // the previous tile's results, stored during the next tile
+  float prev_res[NR];
+#pragma unroll
+  for (int r = 0; r < NR; r++) {
+    prev_key[r] = k1;  // nothing to store before the first tile
+    prev_res[r] = 0.f;
+  }
   CLSA_ISSUE(k0, tile0)
   for (int base = k0; base < kend; base += 2 * kKT) {  // uniform over the workgroup
     CLSA_TILE(base, tile0, tile1)
     if (base + kKT >= kend) break;
     CLSA_TILE(base + kKT, tile1, tile0)
   }
-  if (active && prev_key < k1) srow[prev_key] = prev_key < vis ? prev_res : -INFINITY;
+#pragma unroll
+  for (int r = 0; r < NR; r++)
+    if (active && prev_key[r] < k1) srow[prev_key[r]] = prev_key[r] < vis ? prev_res[r] : -INFINITY;
 #undef CLSA_TILE
 #undef CLSA_ISSUE
 #undef CLSA_CHUNK_AT
@@ -333,6 +385,7 @@ int launch_mfma(const void* q, const void* k, const float* w, float* scores, int
     // 16384; on 2 x 2048 queries x 65536 keys 3.02 ms (8192) against 3.29 (512).
     const int groups = B * ((T + kQB - 1) / kQB);
     int splits = (4096 + groups - 1) / groups;
+    constexpr int kKT = key_tile(DI * IdxElem<DT>::bytes);
     const int max_splits = (kv_len + kKT * 8 - 1) / (kKT * 8);  // at least 8 tiles per split
     if (splits > max_splits) splits = max_splits;
     if (splits < 1) splits = 1;
