@@ -247,6 +247,8 @@ def main():
                          "after evicting the caches) and exit: the run a profiler wraps")
     ap.add_argument("--no-contrast", action="store_true",
                     help="skip the per-layer-indexer (every layer F) step used as the method's contrast")
+    ap.add_argument("--batch-curve", type=lambda x: [int(v) for v in x.split(",") if v], default=[4, 8, 16, 32],
+                    help="batch sizes of the attention-call curve (decode; empty to skip)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -437,7 +439,7 @@ def main():
     idx = step.idx
     topk_ws = torch.empty(clsa.workspace_bytes(0, B=wl.B, T=wl.T, kv_len=wl.kv_len, k=wl.k),
                           dtype=torch.uint8, device="cuda")
-    attn_ws = torch.empty(max(256, clsa.workspace_bytes(1, B=wl.B, T=wl.T, Hq=wl.Hq, Hkv=wl.Hkv, D=wl.D,
+    attn_ws = torch.zeros(max(256, clsa.workspace_bytes(1, B=wl.B, T=wl.T, Hq=wl.Hq, Hkv=wl.Hkv, D=wl.D,
                                                         k=wl.k)), dtype=torch.uint8, device="cuda")
     out = [torch.empty_like(X.q[l]) for l in range(n)]
     lse = [torch.empty((wl.B, wl.T, wl.Hq), dtype=torch.float32, device="cuda") for _ in range(n)]
@@ -517,6 +519,30 @@ def main():
     us_attn_cold = cold_us(lambda i: clsa.sparse_attn(X.q[i % n], X.k_cache[i % n], X.v_cache[i % n], idx,
                                                       kv_len=wl.kv_len, out=out[i % n], lse=lse[i % n],
                                                       ws=attn_ws), 20)
+
+    # The first layer of a real step finds its index and queries in cache
+    # (the top-k and the previous layer just wrote them) and only its rows
+    # cold: the same eviction, then the index and the query re-read.
+    def cold_rows_only(i):
+        evict_caches(scratch)
+        idx.sum()
+        X.q[i % n].float().sum()
+
+    def cold_rows_us(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ts = []
+        for i in range(reps + 2):
+            cold_rows_only(i)
+            a.record()
+            clsa.sparse_attn(X.q[i % n], X.k_cache[i % n], X.v_cache[i % n], idx, kv_len=wl.kv_len,
+                             out=out[i % n], lse=lse[i % n], ws=attn_ws)
+            b.record()
+            torch.cuda.synchronize()
+            if i >= 2:
+                ts.append(a.elapsed_time(b) * 1e3)
+        return statistics.median(ts)
+
+    us_attn_cold_rows = cold_rows_us(20) if wl.T == 1 else None
     us_step_cold = cold_us(lambda i: step.run(), 10)
 
     # Measured memory ceiling on this device: a plain device-to-device copy of
@@ -558,6 +584,37 @@ def main():
         dense = {"k": wl.kv_len, "us": us_dense, "gbs": dense_bytes / (us_dense * 1e-6) / 1e9,
                  "speedup_sparse_vs_dense": us_dense / us_attn}
         del idx_all, ws_all
+    # Attention call against batch size at this context and k (decode): the
+    # call's fixed costs (launch, index latency, split merge) amortise over
+    # more gathered rows as B grows. Caches of B sequences, Gaussian, rows
+    # from a seeded random index; warm (back-to-back) and cold per call.
+    batch_curve = None
+    if wl.T == 1 and args.batch_curve:
+        batch_curve = []
+        for Bc in args.batch_curve:
+            kc_b = inp.randn((Bc, wl.kv_len, wl.Hkv, wl.D), wl.dtype, 31000 + Bc, "cuda")
+            vc_b = inp.randn((Bc, wl.kv_len, wl.Hkv, wl.D), wl.dtype, 32000 + Bc, "cuda")
+            q_b = inp.randn((Bc, 1, wl.Hq, wl.D), wl.dtype, 33000 + Bc, "cuda")
+            g = torch.Generator(device="cuda").manual_seed(34000 + Bc)
+            idx_b = torch.sort(torch.rand((Bc, 1, wl.kv_len), generator=g, device="cuda").argsort(dim=-1)[..., :wl.k]
+                               .to(torch.int32), dim=-1).values.contiguous()
+            ws_b = torch.zeros(max(256, clsa.workspace_bytes(1, B=Bc, T=1, Hq=wl.Hq, Hkv=wl.Hkv, D=wl.D, k=wl.k)),
+                               dtype=torch.uint8, device="cuda")
+            out_b = torch.empty_like(q_b)
+            lse_b = torch.empty((Bc, 1, wl.Hq), dtype=torch.float32, device="cuda")
+            fn = lambda i: clsa.sparse_attn(q_b, kc_b, vc_b, idx_b, kv_len=wl.kv_len, out=out_b, lse=lse_b, ws=ws_b)
+            warm = per_launch_us(fn)
+            cold = cold_us(fn, 10)
+            byt = (Bc * wl.k * wl.Hkv * wl.D * (2 if wl.dtype == 1 else 4) * 2 + Bc * wl.k * 4
+                   + 2 * Bc * wl.Hq * wl.D * (2 if wl.dtype == 1 else 4) + Bc * wl.Hq * 4)
+            batch_curve.append({"B": Bc, "warm_us": warm, "cold_us": cold,
+                                "cold_gbs": byt / (cold * 1e-6) / 1e9,
+                                "cold_frac": byt / (cold * 1e-6) / 1e9 / HBM_PEAK_GBS,
+                                "warm_infinity_cache_gbs": byt / (warm * 1e-6) / 1e9})
+            del kc_b, vc_b, q_b, idx_b, ws_b, out_b, lse_b
+            torch.cuda.empty_cache()
+        print("[bench] attention batch curve: " + ", ".join(
+            f"B={c['B']} {c['warm_us']:.1f}/{c['cold_us']:.1f} us" for c in batch_curve), file=sys.stderr, flush=True)
     del scratch
     step_bytes = len(wl.f_layers) * (alg["index_score"] + alg["topk"]) + n * alg["sparse_attn"]
     f_layers = wl.f_layers
@@ -630,6 +687,11 @@ def main():
                 "avg_launch_us": us_attn, "achieved": attn_gbs, "unit": "GB/s",
                 "state": "back-to-back calls over one index: the rows come from the 256 MB "
                          "Infinity Cache, as for the 15 layers after a step's first (not HBM traffic)"},
+            "cold_rows_hot_index": {
+                "avg_launch_us": us_attn_cold_rows,
+                "achieved": alg["sparse_attn"] / (us_attn_cold_rows * 1e-6) / 1e9, "unit": "GB/s",
+                "state": "caches evicted, then the index and the query re-read: a step's first layer"},
+            "batch_curve": batch_curve,
         })
     else:
         attn_roof.update({"avg_launch_us": us_attn, "cold_launch_us": us_attn_cold})
