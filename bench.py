@@ -185,9 +185,12 @@ def evict_caches(scratch):
 
 def profile_attn(wl, X, step, mode, reps):
     """R attention calls of the step's first layer shapes over the step's
-    index: back to back ("warm": after the first, rows come from the Infinity
-    Cache) or each after evict_caches ("cold": rows come from HBM). Used under
-    rocprofv3, whose per-kernel averages then describe that state."""
+    index: back to back ("warm": a workgroup finds part of its rows in the L2
+    of the XCD it ran on in the previous call, the rest in the Infinity
+    Cache), each after a 64 MiB read ("l2flush": the L2s hold other data, the
+    Infinity Cache still holds the rows) or each after evict_caches ("cold":
+    rows come from HBM). Used under rocprofv3, whose per-kernel averages then
+    describe that state."""
     import torch
     import token_sparse_attention_clsa_amd as clsa
     n = wl.n_layers
@@ -196,10 +199,13 @@ def profile_attn(wl, X, step, mode, reps):
     out = [torch.empty_like(X.q[l]) for l in range(n)]
     lse = [torch.empty((wl.B, wl.T, wl.Hq), dtype=torch.float32, device="cuda") for _ in range(n)]
     scratch = torch.empty(1 << 28, dtype=torch.float32, device="cuda") if mode == "cold" else None
+    flush = torch.zeros(1 << 24, dtype=torch.float32, device="cuda") if mode == "l2flush" else None
     torch.cuda.synchronize()
     for i in range(reps):
         if scratch is not None:
             evict_caches(scratch)
+        if flush is not None:
+            flush.sum()
         clsa.sparse_attn(X.q[i % n], X.k_cache[i % n], X.v_cache[i % n], step.idx, kv_len=wl.kv_len,
                          out=out[i % n], lse=lse[i % n], ws=ws)
         if scratch is not None:
@@ -242,9 +248,10 @@ def main():
     ap.add_argument("--no-graph", action="store_true", help="skip the HIP-graph replay timing")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="run 3 plain device copies of this many MiB first (counter calibration)")
-    ap.add_argument("--profile-attn", choices=["warm", "cold"], default=None,
-                    help="only run the step once, then R attention calls (back to back, or each "
-                         "after evicting the caches) and exit: the run a profiler wraps")
+    ap.add_argument("--profile-attn", choices=["warm", "l2flush", "cold"], default=None,
+                    help="only run the step once, then R attention calls (back to back, each after "
+                         "a 64 MiB read that replaces the L2s' contents, or each after evicting "
+                         "every cache) and exit: the run a profiler wraps")
     ap.add_argument("--no-contrast", action="store_true",
                     help="skip the per-layer-indexer (every layer F) step used as the method's contrast")
     ap.add_argument("--batch-curve", type=lambda x: [int(v) for v in x.split(",") if v], default=[4, 8, 16, 32],
@@ -610,7 +617,7 @@ def main():
             batch_curve.append({"B": Bc, "warm_us": warm, "cold_us": cold,
                                 "cold_gbs": byt / (cold * 1e-6) / 1e9,
                                 "cold_frac": byt / (cold * 1e-6) / 1e9 / HBM_PEAK_GBS,
-                                "warm_infinity_cache_gbs": byt / (warm * 1e-6) / 1e9})
+                                "warm_gbs": byt / (warm * 1e-6) / 1e9})
             del kc_b, vc_b, q_b, idx_b, ws_b, out_b, lse_b
             torch.cuda.empty_cache()
         print("[bench] attention batch curve: " + ", ".join(
@@ -660,9 +667,10 @@ def main():
     # matrix-core flops instead (q.K and P.V: 4 flops per (query head, entry,
     # element)).
     # A decode call is graded cold: every cache evicted before the call, so
-    # its rows come from HBM (back to back, the 15 layers after a step's first
-    # find them in the 256 MB Infinity Cache; that warm rate is reported
-    # separately and is not an HBM figure).
+    # its rows come from HBM. Back to back over one index (the 15 layers after
+    # a step's first, with one shared cache) a workgroup runs on the same XCD
+    # as in the previous call and finds part of its rows in that XCD's L2;
+    # that warm rate is reported separately and is not an HBM figure.
     if wl.T == 1:
         cold_gbs = alg["sparse_attn"] / (us_attn_cold * 1e-6) / 1e9
         attn_roof = {"bound": "hbm", "achieved": cold_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -683,10 +691,12 @@ def main():
             "launch_state": "cold: L2s and Infinity Cache evicted before each call (median of 20)",
             "measured_copy_gbs": copy_gbs,
             "frac_of_measured_copy": cold_gbs / copy_gbs,
-            "infinity_cache_warm": {
+            "warm_caches": {
                 "avg_launch_us": us_attn, "achieved": attn_gbs, "unit": "GB/s",
-                "state": "back-to-back calls over one index: the rows come from the 256 MB "
-                         "Infinity Cache, as for the 15 layers after a step's first (not HBM traffic)"},
+                "state": "back-to-back calls over one index, as for the 15 layers after a step's "
+                         "first: part of the rows come from the XCDs' L2s (each workgroup runs on "
+                         "the XCD it ran on in the previous call), the rest from the Infinity "
+                         "Cache; not HBM traffic"},
             "cold_rows_hot_index": {
                 "avg_launch_us": us_attn_cold_rows,
                 "achieved": alg["sparse_attn"] / (us_attn_cold_rows * 1e-6) / 1e9, "unit": "GB/s",
@@ -730,17 +740,21 @@ def main():
         "dtype": "bf16" if wl.dtype == 1 else "f32",
         "data": "synthetic",
         "config": {
-            "workload": f"{wl.name}: decode B={wl.B}, kv_len={wl.kv_len}, indexer {wl.H_I}x{wl.D_I} "
-                        f"{inp.DTYPE_NAME[wl.idx_dtype]}, top-k {wl.k}, {n} layers sharing one index "
-                        f"({len(f_layers)} indexer pass), GQA {wl.Hq}q/{wl.Hkv}kv x {wl.D}",
+            "workload": f"{wl.name}: {'decode' if wl.T == 1 else 'prefill chunk'} B={wl.B}, T={wl.T}, "
+                        f"kv_len={wl.kv_len}, indexer {wl.H_I}x{wl.D_I} {inp.DTYPE_NAME[wl.idx_dtype]}, "
+                        f"top-k {wl.k}, {n} layers, {len(f_layers)} indexer "
+                        f"pass{'es' if len(f_layers) > 1 else ''} (each F layer's index serves the layers "
+                        f"up to the next F layer), GQA {wl.Hq}q/{wl.Hkv}kv x {wl.D}, "
+                        f"{'one KV cache shared by every layer' if wl.shared_kv else 'a KV cache per layer'}",
             "variant": args.variant,
             "query_sets": N_ROT,
             "global_batch": wl.B,
             "seq_len": wl.kv_len,
             "parallelism": "single GPU",
         },
-        # algorithmic bytes of the whole step over its time; most of a step's
-        # gathers are served by the Infinity Cache, so this is not HBM traffic
+        # algorithmic bytes of the whole step over its time; with one shared
+        # cache the layers after the first re-gather the rows the first one
+        # gathered, part of them from the L2s, so this is not HBM traffic
         "algorithmic_gbs_step": step_bytes / (ms_per_step * 1e-3) / 1e9,
         "roofline": roofline,
         "kernels_us": {
