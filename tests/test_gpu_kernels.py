@@ -51,6 +51,8 @@ IDX_CASES = [
     (inp.FP8_E4M3FN, 2, 9, 48, 64, 600, 640, 4),
     (inp.BF16, 1, 64, 16, 128, 700, 700, 4),     # kv_len close to T: short visible rows
     (inp.BF16, 1, 40, 64, 128, 40, 40, 4),       # T == kv_len: query 0 sees one key
+    (inp.BF16, 2, 12, 32, 128, 1500, 1600, 4),   # multi-query form, 32 heads, L_cap > kv_len
+    (inp.BF16, 1, 9, 64, 128, 1100, 1100, 4),    # multi-query form, 64 heads, a partial group of queries
 ]
 
 
@@ -66,9 +68,10 @@ def test_index_score_integer_inputs_bit_exact(dt, B, T, H, DI, L, cap, m):
     assert np.array_equal(s.cpu().numpy().astype(np.float64), ref)
 
 
-@pytest.mark.parametrize("dt", [inp.BF16, inp.FP8_E4M3FN])
-def test_index_score_gaussian_within_float32_bound(dt):
-    B, T, H, DI, L = 2, 2, 64, 128, 3000
+@pytest.mark.parametrize("dt,T", [(inp.BF16, 2), (inp.FP8_E4M3FN, 2), (inp.BF16, 16), (inp.FP8_E4M3FN, 16)])
+def test_index_score_gaussian_within_float32_bound(dt, T):
+    # T = 2: the decode form; T = 16: the multi-query (LDS-tiled) form
+    B, H, DI, L = 2, 64, 128, 3000
     announce("index_score gauss", inp.DTYPE_NAME[dt], B, T, H, DI, L)
     q = inp.randn((B, T, H, DI), dt, 21, DEV)
     k = inp.randn((B, L, DI), dt, 22, DEV)
