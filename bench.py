@@ -261,7 +261,7 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}, WORLD_SIZE {world}); "
-              "the shared-index decode step is not sharded across GPUs in this build",
+              "the library runs the shared-index decode step on one GPU and does not shard it",
               file=sys.stderr)
         sys.exit(2)
 

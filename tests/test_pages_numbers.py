@@ -2,7 +2,7 @@
 
 The pages give no worked example of the method itself, but several of their
 headline figures are ratios of two printed numbers; these tests check that the
-figures used to size this build's workloads agree with each other. They test
+figures used to size the benchmark workloads agree with each other. They test
 the pages' arithmetic, not the library.
 """
 
