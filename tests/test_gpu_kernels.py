@@ -130,6 +130,11 @@ TOPK_CASES = [
     ("gauss", 1, 1024, 65536, 2048),   # 2 chunks per filter workgroup
     ("ties", 1, 512, 131072, 2048),    # 2 chunks per workgroup, giant tie classes
     ("needle", 2, 600, 66000, 1000),   # 2 chunks per workgroup, a ragged last chunk
+    # Large k: at twice the k-th rank a 4096-chunk holds about 1024 candidates,
+    # the size of its segment, so rows overflow it and are redone from their
+    # scores, with more candidates than the selection keeps in LDS.
+    ("gauss", 1, 1, 131072, 16384),
+    ("needle", 2, 1, 65536, 8192),
 ]
 
 
@@ -172,6 +177,9 @@ ATTN_CASES = [
     # split states (the chunked-prefill plan): 64 and 128 steps of 32 entries
     (inp.BF16, 1, 256, 32, 8, 8192, 8192, 2048),
     (inp.BF16, 1, 300, 32, 8, 9000, 9100, 4096),
+    # large k: the plan's maximum of 256 splits, the combine's largest merge
+    (inp.BF16, 1, 1, 32, 8, 20000, 20000, 16384),
+    (inp.F32, 1, 1, 8, 2, 12000, 12000, 9000),
 ]
 
 
