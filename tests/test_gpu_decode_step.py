@@ -54,6 +54,9 @@ REDUCED = [
     ("prefill2k", dict(T=16, kv_len=3000, k=1024)),
     ("decode32k", dict(B=1, kv_len=1500, k=2048, layer_src=[0, 0])),   # k above kv_len: padding
     ("prefill2k", dict(T=64, kv_len=64, k=16)),                         # query 0 sees one position
+    # three new tokens per step (causal rows through the decode indexer and the
+    # one-launch top-k), two F layers over one shared cache
+    ("decode128k", dict(B=2, T=3, kv_len=9000, layer_src=[0, 0, 2, 2])),
 ]
 
 
