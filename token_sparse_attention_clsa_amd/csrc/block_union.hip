@@ -63,7 +63,7 @@ __global__ __launch_bounds__(kCompactThreads) void union_compact(const uint32_t*
         for (int g = 0; g < Hkv; g++) indices[base + g * nb + off] = i;
       run += tot;
     }
-    if (threadIdx.x < Hkv) indptr[b * Hkv + threadIdx.x] = base + threadIdx.x * nb;
+    if ((int)threadIdx.x < Hkv) indptr[b * Hkv + threadIdx.x] = base + (int)threadIdx.x * nb;
     base += Hkv * nb;
   }
   if (threadIdx.x == 0) indptr[B * Hkv] = base;

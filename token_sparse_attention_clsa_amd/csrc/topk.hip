@@ -477,7 +477,7 @@ __global__ __launch_bounds__(kFilterThreads) void topk_filter(const float* __res
 #pragma unroll
   for (int j = 0; j < kPer; j++) {
     sk[j] = score_key(sv[j]);
-    if (threadIdx.x + j * kFilterThreads < m) {
+    if ((int)threadIdx.x + j * kFilterThreads < m) {
       mn = min(mn, sk[j]);
       mx = max(mx, sk[j]);
     }
@@ -502,7 +502,7 @@ __global__ __launch_bounds__(kFilterThreads) void topk_filter(const float* __res
   const int nb = 1 << (bits - sh);
 #pragma unroll
   for (int j = 0; j < kPer; j++)
-    if (threadIdx.x + j * kFilterThreads < m) atomicAdd(&h[(sk[j] - mn) >> sh], 1u);
+    if ((int)threadIdx.x + j * kFilterThreads < m) atomicAdd(&h[(sk[j] - mn) >> sh], 1u);
   __syncthreads();
   const long expect = ((long)k * m + vis - 1) / vis;  // rank of the k-th key in the sample
   const int r = (int)min((long)m, 2 * expect + 8);
@@ -792,7 +792,7 @@ __global__ __launch_bounds__(kThreads) void topk_fused(const float* __restrict__
 #pragma unroll
     for (int j = 0; j < kPer; j++) {
       sk[j] = score_key(sv[j]);
-      if (threadIdx.x + j * kThreads < m) {
+      if ((int)threadIdx.x + j * kThreads < m) {
         mn = min(mn, sk[j]);
         mx = max(mx, sk[j]);
       }
@@ -805,7 +805,7 @@ __global__ __launch_bounds__(kThreads) void topk_fused(const float* __restrict__
     const int nb = 1 << (bits - sh);
 #pragma unroll
     for (int j = 0; j < kPer; j++)
-      if (threadIdx.x + j * kThreads < m) atomicAdd(&h[(sk[j] - mn) >> sh], 1u);
+      if ((int)threadIdx.x + j * kThreads < m) atomicAdd(&h[(sk[j] - mn) >> sh], 1u);
     __syncthreads();
     const long expect = ((long)kr * m + vis - 1) / vis;  // rank of the k-th key in the sample
     find_bin<kThreads>(h, nb, (int)min((long)m, 2 * expect + 8), res, tmp);
@@ -945,7 +945,7 @@ __global__ __launch_bounds__(kThreads) void topk_lds(const float* __restrict__ s
   const int nb = 1 << (bits - sh);
 #pragma unroll
   for (int j = 0; j < kPer; j++)
-    if (threadIdx.x + j * kThreads < m) atomicAdd(&h[(sk[j] - smn) >> sh], 1u);
+    if ((int)threadIdx.x + j * kThreads < m) atomicAdd(&h[(sk[j] - smn) >> sh], 1u);
   __syncthreads();
   const long expect = ((long)k * m + vis - 1) / vis;  // rank of the k-th key in the sample
   find_bin<kThreads>(h, nb, (int)min((long)m, 2 * expect + 8), res, tmp);
