@@ -30,6 +30,14 @@ namespace clsa {
 namespace {
 
 constexpr int kIdxThreads = 256;  // 4 waves
+
+// This workgroup's share of clearing n words at p: workgroup g of the 2-D
+// grid clears words g * nt + t, g * nt + t + G * nt, ... (G workgroups of nt
+// threads), so no workgroup carries the whole clear.
+__device__ __forceinline__ void zero_share(uint32_t* p, int n, int nt) {
+  const int G = gridDim.x * gridDim.y, g = blockIdx.y * gridDim.x + blockIdx.x;
+  for (int i = g * nt + (int)threadIdx.x; i < n; i += G * nt) p[i] = 0u;
+}
 constexpr int kKeysPerWaveIter = 64;  // 4 MFMA tiles of 16 keys
 
 // max(x, 0) on the bit pattern: a non-negative float's bits are a
@@ -87,10 +95,10 @@ __global__ __launch_bounds__(kIdxThreads) void idx_score_mfma(
     const float* __restrict__ w, float* __restrict__ scores, int T, int kv_len, int L_cap,
     int keys_per_wg, uint32_t* __restrict__ zero_p, int zero_n) {
   using E = IdxElem<DT>;
-  // Words the step's next kernel needs zero (top-k arrival words): cleared
-  // here, so that kernel needs no launch of its own for it.
-  if (zero_n && blockIdx.x == 0 && blockIdx.y == 0)
-    for (int i = threadIdx.x; i < zero_n; i += kIdxThreads) zero_p[i] = 0u;
+  // Words the step's next kernel needs zero (the one-launch top-k's arrival
+  // region): cleared here, a share per workgroup, so that kernel needs no
+  // launch of its own for it.
+  if (zero_n) zero_share(zero_p, zero_n, kIdxThreads);
   constexpr int NS = DI / 32;          // k-steps per key row
   constexpr int NH = HI / 16;          // head tiles
   constexpr int SPAN = DI / 4 * E::bytes;  // bytes of a key row per lane
@@ -208,8 +216,7 @@ __global__ __launch_bounds__(kQB * kWave) void idx_score_multi(
     const float* __restrict__ w, float* __restrict__ scores, int T, int kv_len, int L_cap,
     int keys_per_split, uint32_t* __restrict__ zero_p, int zero_n) {
   using E = IdxElem<DT>;
-  if (zero_n && blockIdx.x == 0 && blockIdx.y == 0)
-    for (int i = threadIdx.x; i < zero_n; i += kQB * kWave) zero_p[i] = 0u;
+  if (zero_n) zero_share(zero_p, zero_n, kQB * kWave);
   constexpr int NS = DI / 32;
   constexpr int NH = HI / 16;
   constexpr int ROWB = DI * E::bytes;          // bytes of one key row: 64, 128 or 256
@@ -350,8 +357,7 @@ __global__ __launch_bounds__(kF32Threads) void idx_score_f32(const float* __rest
                                                      int D, int kv_len, int L_cap,
                                                      uint32_t* __restrict__ zero_p, int zero_n) {
   extern __shared__ float sh[];
-  if (zero_n && blockIdx.x == 0 && blockIdx.y == 0)
-    for (int i = threadIdx.x; i < zero_n; i += kF32Threads) zero_p[i] = 0u;
+  if (zero_n) zero_share(zero_p, zero_n, kF32Threads);
   const int bt = blockIdx.y;
   const int b = bt / T, t = bt % T;
   const int vis = kv_len - T + t + 1;

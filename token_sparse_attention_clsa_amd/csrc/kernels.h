@@ -42,8 +42,9 @@ struct TopkBuffers {
   size_t counts_words, cand_words, spill_words, arrival_words;
 };
 TopkBuffers topk_buffers(int rows, int kv_len);
-// Whether launch_topk takes the one-launch path, whose arrival words
-// (arrival_words u32) must be zero before the launch (it leaves them zero).
+// Whether launch_topk takes the one-launch path, whose arrival region
+// (arrival_words u32: per row an arrival word and a candidate histogram)
+// must be zero before every launch.
 bool topk_uses_arrivals(int rows, int kv_len, int k);
 // k_rows: NULL, or a device int32 [B*T] of per-row counts (clamped to [0, k]).
 // margin: +inf, or the ordered-skipping margin (>= 0): each row keeps only the

@@ -59,6 +59,8 @@ constexpr int kTile = 16384;       // fallback tile: 16 waves x 1024 consecutive
 constexpr int kLdsCap = 12288;     // candidates kept in LDS
 constexpr int kHistCopies = 2;     // fallback histogram copies
 constexpr int kLdsRow = 16384;     // rows up to this length: one launch, row in LDS
+constexpr int kArrStride = 32 + kTopkBins;  // topk_fused: u32 words per row (arrival word, row histogram)
+static_assert(kThreads * 4 == kBins0, "the selection holds the row histogram as 4 bins per thread");
 constexpr int kFusedMaxRows = 64;    // topk_fused: at most this many rows ...
 constexpr int kFusedMaxChunks = 64;  // ... of at most this many 4096-element chunks
 
@@ -71,7 +73,7 @@ constexpr int kFusedMaxChunks = 64;  // ... of at most this many 4096-element ch
 // bin b. Every thread of the block must call it; need must be in [1, total];
 // tmp is int[16]; NT = the block size.
 template <int NT>
-__device__ void find_bin(const uint32_t* h, int nbins, int need, int* res, int* tmp) {
+__device__ __forceinline__ void find_bin(const uint32_t* h, int nbins, int need, int* res, int* tmp) {
   const int per = (nbins + NT - 1) / NT;
   const int hi = nbins - 1 - (int)threadIdx.x * per;
   int sum = 0;
@@ -167,6 +169,32 @@ struct SegCand {
   __device__ uint32_t k(int i) const { return (uint32_t)e(i).y; }
 };
 
+// One wave ranks the cnt <= 64 keys in few[] (keys strictly above and
+// equal to each): res[0] = the need-th largest (theta), res[1] = how many
+// keys equal to theta are still to take. Every thread calls it; the first
+// wave works. need must be in [1, cnt].
+__device__ __forceinline__ void rank_few(const uint32_t* few, int cnt, int need, int* res) {
+  if (threadIdx.x < kWave) {
+    const int lane = threadIdx.x;
+    const uint32_t v = lane < cnt ? few[lane] : 0u;
+    int gt = 0, eq = 0;
+    for (int j = 0; j < cnt; j++) {  // uniform
+      const uint32_t o = (uint32_t)__builtin_amdgcn_readlane((int)v, j);
+      gt += o > v;
+      eq += o == v;
+    }
+    const unsigned long long hit = __ballot(lane < cnt && gt < need && need <= gt + eq);
+    if (lane == __builtin_ctzll(hit)) {
+      res[0] = (int)v;     // theta
+      res[1] = need - gt;  // keys equal to theta still to take
+    }
+  }
+}
+
+template <class Acc>
+__device__ void emit_selection(const Acc& acc, int n, uint32_t theta, int quota, int* tmp, int32_t* out,
+                               int k, int32_t* kept);
+
 // Resolves theta, the need-th largest key among the candidates, all of
 // which in play lie in [lo, lo + R) (R a power of two <= 2^32), by radix
 // passes of at most 12 bits on key - lo, then emits the row's selection:
@@ -205,21 +233,7 @@ __device__ void select_and_emit(const Acc& acc, int n, int need, uint32_t lo, ui
         if (key >= lo && (uint64_t)(key - lo) < R) few[atomicAdd(&nfew, 1)] = key;
       }
       __syncthreads();
-      if (threadIdx.x < kWave) {
-        const int lane = threadIdx.x;
-        const uint32_t v = lane < cnt ? few[lane] : 0u;
-        int gt = 0, eq = 0;
-        for (int j = 0; j < cnt; j++) {  // uniform
-          const uint32_t o = (uint32_t)__builtin_amdgcn_readlane((int)v, j);
-          gt += o > v;
-          eq += o == v;
-        }
-        const unsigned long long hit = __ballot(lane < cnt && gt < need && need <= gt + eq);
-        if (lane == __builtin_ctzll(hit)) {
-          res[0] = (int)v;     // theta
-          res[1] = need - gt;  // keys equal to theta still to take
-        }
-      }
+      rank_few(few, cnt, need, res);
       __syncthreads();
       lo = (uint32_t)res[0];
       need = res[1];
@@ -232,9 +246,18 @@ __device__ void select_and_emit(const Acc& acc, int n, int need, uint32_t lo, ui
     theta = mkey;
     quota = INT_MAX;
   }
-  // Ordered emission: thread t owns the run [t0 + t * run, t0 + (t + 1) * run)
-  // of the tile (run <= 16), so up to 16 * kThreads candidates take one
-  // block scan and no barrier waits behind the output stores.
+  emit_selection(acc, n, theta, quota, tmp, out, k, kept);
+}
+
+// Ordered emission of a row's selection: keys above theta always, keys equal
+// to theta for the first `quota` of them in candidate (position) order; the
+// slots past the kept count hold -1 and kept (or NULL) receives the count.
+// Thread t owns the run [t0 + t * run, t0 + (t + 1) * run) of the tile
+// (run <= 16), so up to 16 * kThreads candidates take one block scan and no
+// barrier waits behind the output stores.
+template <class Acc>
+__device__ void emit_selection(const Acc& acc, int n, uint32_t theta, int quota, int* tmp, int32_t* out,
+                               int k, int32_t* kept) {
   const int run = min(16, max(1, (n + kThreads - 1) / kThreads));
   int gt_base = 0, eq_base = 0;
   for (int t0 = 0; t0 < n; t0 += run * kThreads) {  // uniform over the workgroup
@@ -287,7 +310,7 @@ __device__ void select_top(const Acc& acc, int n, int k, uint32_t mn, uint32_t m
 
 // Block-wide min and max of the threads' (mn, mx); ends with a barrier
 // (the writes before it, e.g. an LDS gather, are visible after it).
-__device__ void block_minmax(uint32_t& mn, uint32_t& mx, uint32_t (*mm)[kWaves]) {
+__device__ __forceinline__ void block_minmax(uint32_t& mn, uint32_t& mx, uint32_t (*mm)[kWaves]) {
   mn = wave_min_u32(mn);
   mx = wave_max_u32(mx);
   const int wave = threadIdx.x / kWave;
@@ -586,6 +609,8 @@ __device__ bool row_prologue(const float* srow, int vis, int& k, const int32_t* 
 // LDS of the selection (one 1024-thread workgroup per row).
 struct SelectLds {
   uint32_t h[kBins0 * (1 + kHistCopies)];
+  uint32_t few[kWave];  // keys of the k-th key's bin (row-histogram path)
+  int nfew;
   int32_t lpos[kLdsCap];
   uint32_t lkey[kLdsCap];
   int off[kTopkMaxChunks + 1];
@@ -598,11 +623,21 @@ struct SelectLds {
 // Selection of row `row` from the filter's candidate segments (counts at
 // counts[row * cstride + c]); every thread of the 1024-thread workgroup
 // calls it. trust_segments false: redo the row from its scores alone.
+// ghist (or NULL): the row's histogram of its candidates, gnb bins of 2^gs
+// keys from key gthr, the last bin also holding every key above them (built
+// by the one-launch filter). With it, the bin of the k-th key comes straight
+// from the histogram, and the selection resolves the k-th key inside that
+// bin only: up to 64 keys are collected while the candidates are gathered
+// and ranked by one wave, more take radix passes over the bin's key range.
+// The general path (the candidates' key range, radix passes over it) takes
+// over when that bin is the open last one or the row is cut by a margin
+// (which needs the row maximum).
 __device__ __forceinline__ void select_row(int row, const float* __restrict__ scores, const uint32_t* __restrict__ counts,
                            int cstride, const int2* __restrict__ cand, int32_t* __restrict__ spill,
                            int32_t* __restrict__ idx, int T, int kv_len, int k,
                            const int32_t* __restrict__ k_rows, int nchunks, float margin,
-                           int32_t* __restrict__ kept, bool trust_segments, SelectLds& L) {
+                           int32_t* __restrict__ kept, bool trust_segments, const uint32_t* ghist,
+                           uint32_t gthr, int gs, int gnb, SelectLds& L) {
   uint32_t* h = L.h;
   int32_t* lpos = L.lpos;
   uint32_t* lkey = L.lkey;
@@ -617,6 +652,14 @@ __device__ __forceinline__ void select_row(int row, const float* __restrict__ sc
   const float* srow = scores + (size_t)row * kv_len;
   if (row_prologue(srow, vis, k, k_rows, row, margin, out, kept_row, mm, tmp)) return;
   const bool skip = margin < INFINITY;  // ordered skipping (uniform)
+  const bool use_hist = ghist != nullptr && !skip && gnb > 1;  // uniform
+  // Thread t holds bins 4 (1023 - t) .. 4 (1023 - t) + 3 (kThreads * 4 =
+  // kBins0), so the threads in order run from the highest bins down.
+  // The counts and the histogram are loaded first: the scan below waits
+  // only for them, while the speculative gather loads are still arriving.
+  const int v = (int)threadIdx.x < nchunks ? (int)counts[(size_t)row * cstride + threadIdx.x] : 0;
+  uint4 gh = make_uint4(0u, 0u, 0u, 0u);
+  if (use_hist) gh = reinterpret_cast<const uint4*>(ghist)[kThreads - 1 - threadIdx.x];
   // Chunk owned by this thread for the gather: tpc threads per chunk, thread
   // j0 of a chunk takes entries j0, j0 + tpc, ... Its first kSpec entries are
   // loaded now, before the counts are known (the slots exist whatever the
@@ -628,24 +671,106 @@ __device__ __forceinline__ void select_row(int row, const float* __restrict__ sc
   constexpr int kSpec = 8;
   int2 pre[kSpec];
 #pragma unroll
-  for (int u = 0; u < kSpec; u++) {
-    const int j = j0 + u * tpc;
-    pre[u] = j < kTopkSegCap ? sg[j] : make_int2(0, 0);
-  }
-  // Offsets of the candidate segments.
+  for (int u = 0; u < kSpec; u++)  // unconditional (clamped) loads: all in flight together
+    pre[u] = sg[min(j0 + u * tpc, kTopkSegCap - 1)];  // used only where j0 + u * tpc < count <= kTopkSegCap
+  if (use_hist && threadIdx.x == 0) L.nfew = 0;  // published by the barriers below
+  // Offsets of the candidate segments, whether a segment overflowed, and
+  // (with the row histogram) the bin of the k-th key: one block scan of the
+  // counts and of the bin sums together.
   int n;
   bool overflow;
+  int fb = -1, hab = 0, cb = 0;  // bin of the k-th key, keys above it, keys in it (fb < 0: none)
   {
     const int c = threadIdx.x;
-    const int v = c < nchunks ? (int)counts[(size_t)row * cstride + c] : 0;
-    const int o = block_exclusive_scan<kThreads>(v, tmp, &n);
-    if (c < nchunks) off[c] = o;
+    const int lane = c % kWave;
+    const int wid = __builtin_amdgcn_readfirstlane(c / kWave);
+    const int hs = (int)(gh.x + gh.y + gh.z + gh.w);
+    const int inc = wave_inclusive_scan(v), hinc = wave_inclusive_scan(hs);
+    const bool wave_ovf = __ballot(v > kTopkSegCap) != 0;
+    if (lane == kWave - 1) {
+      tmp[wid] = inc;
+      wtot[wid] = hinc;
+      mm[0][wid] = wave_ovf;
+    }
+    __syncthreads();
+    const int x = lane < kWaves ? tmp[lane] : 0, hx = lane < kWaves ? wtot[lane] : 0;
+    const int xs = wave_inclusive_scan(x), hxs = wave_inclusive_scan(hx);
+    overflow = __ballot(lane < kWaves && mm[0][lane] != 0u) != 0;
+    n = __builtin_amdgcn_readlane(xs, kWaves - 1);
+    if (c < nchunks) off[c] = __builtin_amdgcn_readlane(xs - x, wid) + inc - v;
     if (c == 0) off[nchunks] = n;
-    overflow = __syncthreads_or(v > kTopkSegCap) != 0;
+    const int htot = __builtin_amdgcn_readlane(hxs, kWaves - 1);  // n, when the segments are trusted
+    const bool hit = use_hist && k > 0 && htot >= k;             // uniform
+    if (hit) {
+      int acc = __builtin_amdgcn_readlane(hxs - hx, wid) + hinc - hs;  // keys in the bins above this thread's
+      if (acc < k && k <= acc + hs) {  // the k-th key is in one of this thread's bins
+        const int b3 = 4 * (kThreads - 1 - c) + 3;
+        const uint32_t cnt[4] = {gh.w, gh.z, gh.y, gh.x};
+        for (int j = 0; j < 4; j++) {
+          if (acc + (int)cnt[j] >= k) {
+            res[0] = b3 - j;
+            res[1] = acc;
+            res[2] = (int)cnt[j];
+            break;
+          }
+          acc += (int)cnt[j];
+        }
+      }
+    }
+    __syncthreads();  // publishes off and res
+    if (hit) {
+      fb = res[0];
+      hab = res[1];
+      cb = res[2];
+      if (fb >= gnb - 1) fb = -1;  // the open last bin: general path (uniform)
+    }
   }
   if (n >= k && !overflow && trust_segments) {
     uint32_t mn = 0xffffffffu, mx = 0u;  // key range of the candidates
     if (n <= kLdsCap) {
+      if (fb >= 0) {
+        // The k-th key lies in [blo, bhi), with hab candidates above it.
+        // Up to 64 keys there are collected during the gather and ranked by
+        // one wave; more take radix passes over that range only.
+        const uint64_t blo = (uint64_t)gthr + ((uint64_t)fb << gs), bhi = blo + (1ull << gs);
+        const uint64_t flo = cb <= kWave ? blo : bhi;  // collect nothing past 64 keys
+        if (gc < nchunks) {
+          const int o = off[gc], cnt = off[gc + 1] - off[gc];
+#pragma unroll
+          for (int u = 0; u < kSpec; u++) {
+            const int j = j0 + u * tpc;
+            if (j < cnt) {
+              const uint32_t key = (uint32_t)pre[u].y;
+              lpos[o + j] = pre[u].x;
+              lkey[o + j] = key;
+              if (key >= flo && key < bhi) {
+                const int f = atomicAdd(&L.nfew, 1);
+                if (f < kWave) L.few[f] = key;  // cb <= kWave of them
+              }
+            }
+          }
+          for (int j = j0 + kSpec * tpc; j < cnt; j += tpc) {
+            const int2 e = sg[j];
+            const uint32_t key = (uint32_t)e.y;
+            lpos[o + j] = e.x;
+            lkey[o + j] = key;
+            if (key >= flo && key < bhi) {
+              const int f = atomicAdd(&L.nfew, 1);
+              if (f < kWave) L.few[f] = key;
+            }
+          }
+        }
+        __syncthreads();  // the candidates (and the bin's keys) are in LDS
+        const Cand acc{lpos, lkey, nullptr, srow};
+        if (cb <= kWave) {
+          rank_few(L.few, cb, k - hab, res);
+          __syncthreads();
+          emit_selection(acc, n, (uint32_t)res[0], res[1], tmp, out, k, kept_row);
+        } else {
+          select_and_emit(acc, n, k - hab, (uint32_t)blo, 1ull << gs, h, res, tmp, out, k, 0u, kept_row);
+        }
+        return;
+      }
       if (gc < nchunks) {
         const int o = off[gc], cnt = off[gc + 1] - off[gc];
 #pragma unroll
@@ -713,7 +838,7 @@ __global__ __launch_bounds__(kThreads) void topk_select(const float* __restrict_
                                                         int32_t* __restrict__ kept) {
   __shared__ __attribute__((aligned(16))) SelectLds L;
   select_row(blockIdx.x, scores, counts, cstride, cand, spill, idx, T, kv_len, k, k_rows, nchunks, margin,
-             kept, true, L);
+             kept, true, nullptr, 0u, 0, 0, L);
 }
 
 
@@ -733,9 +858,11 @@ __global__ __launch_bounds__(kThreads) void topk_select(const float* __restrict_
 // three fields; the sums equal (n x, n x^2) only when all n arrivals ran on
 // XCD x. Otherwise the last arrival redoes the row from its scores alone
 // (the select's full-row path), which reads nothing the filter wrote.
-// Arrival words: one 64-bit word per row, 128 bytes apart (count bits 0..15,
-// sum of x bits 16..31, sum of x^2 bits 32..63), zero before the launch and
-// reset to zero by the row's last arrival.
+// Arrival region: per row kArrStride u32 words, the 64-bit arrival word
+// first (count bits 0..15, sum of x bits 16..31, sum of x^2 bits 32..63),
+// then from word 32 the row's candidate histogram (4096 u32). The whole
+// region is zero before every launch (the caller clears it; the last
+// arrival also resets its word).
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ uint32_t xcc_id() {
   return __builtin_amdgcn_s_getreg((3 << 11) | 20);  // HW_REG_XCC_ID, bits [3:0]
@@ -750,12 +877,15 @@ __global__ __launch_bounds__(kThreads) void topk_fused(const float* __restrict__
                                                        const int32_t* __restrict__ k_rows, int nchunks,
                                                        int cstride, int cpw, int wpr, int rows, int n_xcd,
                                                        float margin, int32_t* __restrict__ kept,
-                                                       uint64_t* __restrict__ arrivals, int force_redo) {
+                                                       uint32_t* __restrict__ arrivals, int force_redo) {
   __shared__ __attribute__((aligned(16))) SelectLds L;
   __shared__ int s_flag;
   const int x = blockIdx.x % n_xcd, slot = blockIdx.x / n_xcd;
   const int row = x + n_xcd * (slot / wpr);
   if (row >= rows) return;  // no row for this workgroup (uniform)
+  uint32_t* ghist = arrivals + (size_t)row * kArrStride + 32;  // the row's candidate histogram
+  uint32_t gthr = 0u;  // its bins: gnb bins of 2^gs keys from gthr (gnb = 0: not computed here)
+  int gs = 0, gnb = 0;
   const int ci0 = (slot % wpr) * cpw, ci1 = min(nchunks, ci0 + cpw);
   const int vis = kv_len - T + (row % T) + 1;
   const float* srow = scores + (size_t)row * kv_len;
@@ -810,6 +940,20 @@ __global__ __launch_bounds__(kThreads) void topk_fused(const float* __restrict__
     const long expect = ((long)kr * m + vis - 1) / vis;  // rank of the k-th key in the sample
     find_bin<kThreads>(h, nb, (int)min((long)m, 2 * expect + 8), res, tmp);
     const uint32_t thr = mn + ((uint32_t)res[0] << sh);
+    // The row's candidate histogram: at most 4096 bins of 2^gs keys from
+    // thr, reaching the sample's largest key; keys above go to the last bin.
+    // Every workgroup of the row derives the same bins from the same sample.
+    // Each workgroup bins its own candidates in LDS first (the sample's
+    // histogram is no longer read) and adds only its non-zero bins to the
+    // row's, so no bin takes more than one global atomic per workgroup.
+    {
+      const uint64_t gspan = (uint64_t)(mx - thr) + 1;  // thr <= mx: its bin holds a sample key
+      const int gbits = gspan == 1 ? 0 : 64 - __clzll(gspan - 1);
+      gs = gbits > 12 ? gbits - 12 : 0;
+      gnb = 1 << (gbits - gs);
+      gthr = thr;
+    }
+    for (int i = threadIdx.x; i < kBins0; i += kThreads) h[i] = 0u;  // ordered before the adds by the scan's barriers
     for (int ci = ci0; ci < ci1; ci++) {  // uniform over the workgroup
       const int c0 = ci * kChunk;
       if (c0 >= vis) {
@@ -842,16 +986,22 @@ __global__ __launch_bounds__(kThreads) void topk_fused(const float* __restrict__
         if (flags >> j & 1u) {
           if (o < kTopkSegCap) seg[o] = make_int2(e + j, (int)key[j]);
           o++;
+          atomicAdd(&h[min((key[j] - thr) >> gs, (uint32_t)gnb - 1u)], 1u);
         }
       if (threadIdx.x == 0) cnt[ci] = (uint32_t)total;  // above kTopkSegCap: the row is redone
     }
+    __syncthreads();  // the workgroup's bins are complete
+    for (int b = threadIdx.x; b < gnb; b += kThreads) {
+      const uint32_t c = h[b];
+      if (c) atomicAdd(&ghist[b], c);
+    }
   }
-  __builtin_amdgcn_s_waitcnt(0);  // this thread's segment and count stores are done (in this XCD's L2)
+  __builtin_amdgcn_s_waitcnt(0);  // this thread's segment, count and histogram writes are done (in this XCD's L2)
   __syncthreads();
   if (threadIdx.x == 0) {
     const uint64_t xi = xcc_id() & 15u;
     const uint64_t mine = 1ull | (xi << 16) | ((xi * xi) << 32);
-    uint64_t* word = arrivals + (size_t)row * 16;
+    uint64_t* word = reinterpret_cast<uint64_t*>(arrivals + (size_t)row * kArrStride);
     const uint64_t now = __hip_atomic_fetch_add(word, mine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + mine;
     int flag = 0;
     if ((now & 0xffffu) == (uint64_t)wpr) {  // every workgroup of the row has arrived
@@ -865,7 +1015,7 @@ __global__ __launch_bounds__(kThreads) void topk_fused(const float* __restrict__
   __syncthreads();
   if (s_flag == 0) return;
   select_row(row, scores, counts, cstride, cand, spill, idx, T, kv_len, k, k_rows, nchunks, margin, kept,
-             s_flag == 1, L);
+             s_flag == 1, gnb ? ghist : nullptr, gthr, gs, gnb, L);
 }
 
 // A whole row held in LDS as keys.
@@ -979,7 +1129,8 @@ TopkBuffers topk_buffers(int rows, int kv_len) {
   b.counts_words = (size_t)rows * b.cstride;
   b.cand_words = (size_t)rows * b.nchunks * kTopkSegCap * 2;
   b.spill_words = (size_t)rows * kv_len;
-  b.arrival_words = (size_t)rows * 32;  // one 64-bit word per row, 128 bytes apart
+  // per row of the one-launch form (only for few rows): arrival word, row histogram
+  b.arrival_words = rows <= kFusedMaxRows ? (size_t)rows * kArrStride : 0;
   return b;
 }
 
@@ -1043,7 +1194,7 @@ int launch_topk(const float* scores, int B, int T, int kv_len, int k, const int3
     const int rpx = (rows + n_xcd - 1) / n_xcd;
     hipLaunchKernelGGL(topk_fused, dim3((unsigned)(n_xcd * rpx * wpr)), dim3(kThreads), 0, stream, scores,
                        counts, segs, spill, idx, T, kv_len, k, k_rows, tb.nchunks, tb.cstride, 1, wpr,
-                       rows, n_xcd, margin, kept, reinterpret_cast<uint64_t*>(arrivals), force_redo());
+                       rows, n_xcd, margin, kept, arrivals, force_redo());
     return check_launch("topk_fused");
   }
   // Chunks per filter workgroup: one while the grid stays small (decode),
