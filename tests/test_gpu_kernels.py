@@ -135,6 +135,11 @@ TOPK_CASES = [
     # scores, with more candidates than the selection keeps in LDS.
     ("gauss", 1, 1, 131072, 16384),
     ("needle", 2, 1, 65536, 8192),
+    # Small tie classes at the k-th key (a few tens of equal keys): the
+    # selection takes the first of them in position order.
+    ("grid", 4, 1, 131072, 2048),
+    ("grid", 2, 1, 65536, 1000),
+    ("grid", 1, 3, 50000, 2048),
 ]
 
 

@@ -204,7 +204,9 @@ def score_rows(kind: str, B: int, T: int, L: int, seed: int, device="cpu") -> to
     "strided" (every 64th position far above the rest), "sampled" (far
     above the rest exactly at the positions the top-k filter samples for its
     threshold: 128 evenly spaced runs of 16, run j starting at
-    j * (L - 16) // 127; single-query rows, L > 2048).
+    j * (L - 16) // 127; single-query rows, L > 2048), "grid" (N(0,1)
+    rounded to multiples of 1/256: near the k-th largest of a long row each
+    value is shared by a few tens of positions, small tie classes).
     """
     g = _gen(seed, device)
     shape = (B, T, L)
@@ -226,6 +228,8 @@ def score_rows(kind: str, B: int, T: int, L: int, seed: int, device="cpu") -> to
         return torch.where(m, x + 8.0, x)
     if kind == "const":
         return torch.full(shape, 3.5, device=device)
+    if kind == "grid":
+        return torch.round(torch.randn(shape, generator=g, device=device) * 256.0) / 256.0
     if kind == "desc":
         return (-torch.arange(L, device=device, dtype=torch.float32)).expand(shape).contiguous()
     if kind == "strided":  # every 64th position far above the rest
