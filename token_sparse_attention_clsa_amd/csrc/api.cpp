@@ -329,8 +329,9 @@ int clsa_decode_step(const clsa_step_desc* d, void* ws, size_t ws_bytes, void* s
   int32_t* kept = d->k_per_query != nullptr || margin < INFINITY
                       ? reinterpret_cast<int32_t*>(base + L.kept)
                       : nullptr;
-  // The one-launch top-k needs its arrival words zero: each F layer's
-  // indexer kernel clears them before the top-k that follows it runs.
+  // The one-launch top-k needs its arrival region (arrival words and row
+  // histograms) zero: each F layer's indexer kernel clears it before the
+  // top-k that follows it runs.
   ZeroJob zj;
   if (topk_uses_arrivals(d->B * d->T, d->kv_len, d->k)) zj = ZeroJob{arrivals, (int)L.topk.arrival_words};
   for (int l = 0; l < d->n_layers; l++) {
