@@ -140,6 +140,14 @@ TOPK_CASES = [
     ("grid", 4, 1, 131072, 2048),
     ("grid", 2, 1, 65536, 1000),
     ("grid", 1, 3, 50000, 2048),
+    # The one-launch top-k's row histogram: a k-th key in a bin of a few
+    # hundred equal keys (radix passes inside that bin, part of the ties
+    # taken), and a small k whose k-th key lies above the sample's largest
+    # (the open last bin: the general path) or inside the sampled range.
+    ("coarse", 4, 1, 131072, 2048),
+    ("coarse", 2, 1, 65536, 1000),
+    ("gauss", 2, 1, 131072, 16),
+    ("needle", 3, 1, 100000, 64),
 ]
 
 

@@ -206,7 +206,9 @@ def score_rows(kind: str, B: int, T: int, L: int, seed: int, device="cpu") -> to
     threshold: 128 evenly spaced runs of 16, run j starting at
     j * (L - 16) // 127; single-query rows, L > 2048), "grid" (N(0,1)
     rounded to multiples of 1/256: near the k-th largest of a long row each
-    value is shared by a few tens of positions, small tie classes).
+    value is shared by a few tens of positions, small tie classes), "coarse"
+    (N(0,1) rounded to multiples of 1/16: a few hundred positions share the
+    k-th largest value of a long row).
     """
     g = _gen(seed, device)
     shape = (B, T, L)
@@ -230,6 +232,8 @@ def score_rows(kind: str, B: int, T: int, L: int, seed: int, device="cpu") -> to
         return torch.full(shape, 3.5, device=device)
     if kind == "grid":
         return torch.round(torch.randn(shape, generator=g, device=device) * 256.0) / 256.0
+    if kind == "coarse":
+        return torch.round(torch.randn(shape, generator=g, device=device) * 16.0) / 16.0
     if kind == "desc":
         return (-torch.arange(L, device=device, dtype=torch.float32)).expand(shape).contiguous()
     if kind == "strided":  # every 64th position far above the rest
