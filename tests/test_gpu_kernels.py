@@ -148,6 +148,10 @@ TOPK_CASES = [
     ("coarse", 2, 1, 65536, 1000),
     ("gauss", 2, 1, 131072, 16),
     ("needle", 3, 1, 100000, 64),
+    # Many rows through the one-launch form (up to its 64 rows): 16 rows of
+    # 16 chunks, and 48 causal rows of a 40000-position cache.
+    ("gauss", 16, 1, 65536, 2048),
+    ("grid", 1, 48, 40000, 1000),
 ]
 
 
