@@ -279,7 +279,7 @@ def main():
                          "every cache) and exit: the run a profiler wraps")
     ap.add_argument("--no-contrast", action="store_true",
                     help="skip the per-layer-indexer (every layer F) step used as the method's contrast")
-    ap.add_argument("--batch-curve", type=lambda x: [int(v) for v in x.split(",") if v], default=[4, 8, 16, 32],
+    ap.add_argument("--batch-curve", type=lambda x: [int(v) for v in x.split(",") if v], default=[4, 8, 16, 32, 64],
                     help="batch sizes of the attention-call curve (decode; empty to skip)")
     args = ap.parse_args()
 

@@ -197,6 +197,11 @@ ATTN_CASES = [
     # large k: the plan's maximum of 256 splits, the combine's largest merge
     (inp.BF16, 1, 1, 32, 8, 20000, 20000, 16384),
     (inp.F32, 1, 1, 8, 2, 12000, 12000, 9000),
+    # the decode plans of the benchmark's larger batches (the plan depends on
+    # B, T, Hkv and k only): 8 splits of 8 steps per wave (B = 32) and 4
+    # splits of 16 steps per wave (B = 64), k = 2048
+    (inp.BF16, 32, 1, 32, 8, 3000, 3000, 2048),
+    (inp.BF16, 64, 1, 32, 8, 2500, 2600, 2048),
 ]
 
 
