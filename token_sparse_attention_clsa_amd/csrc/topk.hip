@@ -29,6 +29,9 @@
 //      than k or a chunk overflowed its segment, it redoes the row on its own
 //      (LDS histogram of the full row's top 12 bits, ordered candidate pass),
 //      so the result is exact whatever the sample did.
+// Few long rows (decode) take both steps in one launch (topk_fused, below),
+// where the filter also builds each row's candidate histogram and the row's
+// last workgroup selects.
 // Rows whose visible count is <= k take every visible position. With a
 // per-row count k_rows[row] (clamped to [0, k]), a row keeps its k_rows[row]
 // best positions and the rest of its k slots hold -1.
@@ -846,8 +849,10 @@ __global__ __launch_bounds__(kThreads) void topk_select(const float* __restrict_
 // One-launch form for few rows (decode): grid = rows x filter workgroups,
 // 1024 threads each. A workgroup takes cpw consecutive 4096-element chunks
 // of its row, computes the row's sample threshold as topk_filter does and
-// writes the chunks' candidate segments and counts; it then waits until its
-// stores are done and counts itself in the row's arrival word. The
+// writes the chunks' candidate segments and counts, and adds its candidates
+// to the row's candidate histogram (bins from the same sample); it then
+// waits until its stores are done and counts itself in the row's arrival
+// word. The
 // workgroup that arrives last selects the row (topk_select's work) from the
 // segments. Segments and counts are plain stores into the L2 of the
 // writer's XCD; the selecting workgroup reads them through its own L2, so
