@@ -386,6 +386,37 @@ def main():
         graph_ms = (time.perf_counter() - t2) * 1e3 / (reps * N_ROT)
         print(f"[bench] graph replay: {graph_ms * 1e3:.1f} us/step", file=sys.stderr, flush=True)
 
+    # Where a step's time goes: the same steps with events recorded between
+    # their stages (before each F layer's indexer, between it and its top-k,
+    # around every attention call), one step at a time, medians over the
+    # steps. The events themselves add a little to every stage.
+    stage_ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4 * n)] for _ in range(N_ROT)]
+    st_ev = [clsa.DecodeStep(wl.layer_src, q, X.k_cache, X.v_cache, qi, X.k_idx, w, wl.k, kv_len=wl.kv_len,
+                             events=stage_ev[i]) for i, (q, qi, w) in enumerate(qsets)]
+    for st in st_ev:
+        st.run()
+    torch.cuda.synchronize()
+    f_layers_ev = [l for l in range(n) if wl.layer_src[l] == l]
+    t_idx, t_topk, t_a0, t_arest = [], [], [], []
+    for i in range(max(N_ROT, min(K, 40))):
+        st_ev[i % N_ROT].run()
+        torch.cuda.synchronize()
+        e = stage_ev[i % N_ROT]
+        t_idx.append(sum(e[4 * l].elapsed_time(e[4 * l + 1]) for l in f_layers_ev) * 1e3)
+        t_topk.append(sum(e[4 * l + 1].elapsed_time(e[4 * l + 2]) for l in f_layers_ev) * 1e3)
+        t_a0.append(e[2].elapsed_time(e[3]) * 1e3)
+        if n > 1:
+            t_arest.append(statistics.mean(e[4 * l + 2].elapsed_time(e[4 * l + 3]) for l in range(1, n)) * 1e3)
+    step_stages = {"indexer_us": statistics.median(t_idx), "topk_us": statistics.median(t_topk),
+                   "attn_first_layer_us": statistics.median(t_a0),
+                   "attn_other_layers_mean_us": statistics.median(t_arest) if t_arest else None,
+                   "steps": len(t_idx),
+                   "note": "per step: indexer and top-k summed over the F layers; events between the "
+                           "stages, one step at a time (the events add a little to each stage)"}
+    del st_ev, stage_ev
+    print(f"[bench] step stages: indexer {step_stages['indexer_us']:.1f} us, top-k {step_stages['topk_us']:.1f} us, "
+          f"attention {step_stages['attn_first_layer_us']:.1f} us (first layer)", file=sys.stderr, flush=True)
+
     # The same step with a per-query count of kept positions (the dynamic-k
     # reading), counts drawn uniformly from [k/4, k] (seeded): GPU time of K
     # back-to-back steps between one event pair (the wall clock of the first
@@ -832,6 +863,7 @@ def main():
         "ordered_skip": ordered_skip,
         "method_contrast": contrast,
         "ms_per_step_graph_replay": graph_ms,
+        "step_stages_us": step_stages,
     }
     if comparator is not None:
         result["block_union_comparator"] = comparator
