@@ -389,7 +389,8 @@ def main():
     # Where a step's time goes: the same steps with events recorded between
     # their stages (before each F layer's indexer, between it and its top-k,
     # around every attention call), one step at a time, medians over the
-    # steps. The events themselves add a little to every stage.
+    # steps. Each recorded event adds about 1-2 us, so the stages sum to more
+    # than the step.
     stage_ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4 * n)] for _ in range(N_ROT)]
     st_ev = [clsa.DecodeStep(wl.layer_src, q, X.k_cache, X.v_cache, qi, X.k_idx, w, wl.k, kv_len=wl.kv_len,
                              events=stage_ev[i]) for i, (q, qi, w) in enumerate(qsets)]
@@ -412,7 +413,8 @@ def main():
                    "attn_other_layers_mean_us": statistics.median(t_arest) if t_arest else None,
                    "steps": len(t_idx),
                    "note": "per step: indexer and top-k summed over the F layers; events between the "
-                           "stages, one step at a time (the events add a little to each stage)"}
+                           "stages, one step at a time: each recorded event adds about 1-2 us, so the "
+                           "stages sum to more than ms_per_step"}
     del st_ev, stage_ev
     print(f"[bench] step stages: indexer {step_stages['indexer_us']:.1f} us, top-k {step_stages['topk_us']:.1f} us, "
           f"attention {step_stages['attn_first_layer_us']:.1f} us (first layer)", file=sys.stderr, flush=True)
